@@ -1,0 +1,157 @@
+"""CPU oracle for the query-free KV-cache eviction step -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg
+import this package.  The product (``kv_cache_token_amd`` and its HIP library)
+never imports it, and the two share no code: the only common input is the
+seeded generator module ``kv_cache_token_amd.synth``, which holds none of the
+method's arithmetic.
+
+The eviction rules live in ``kvx_oracle.c`` (plain C, fp64 scoring, a plain sort
+for the ranking); this module loads it with ctypes, building it with gcc if the
+shared object is absent.  The calibration rules (query-SVD filter, GQA averaging,
+key-SVD fallback) live in ``calib.py`` and use numpy's SVD.
+
+Pins: every function here is checked by ``tests/test_oracle_*.py`` against
+brute force, closed forms, an independent streaming implementation and the
+invariants the pages state; see the docstrings there.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+from . import calib  # noqa: F401  (re-exported)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvx_oracle.c")
+_LIB = os.path.join(_HERE, "libkvx_oracle.so")
+_lib = None
+
+MODE_L2, MODE_PROJ = 0, 1
+DT_F32, DT_BF16 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle's C source into a shared object next to it."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.orc_score.argtypes = [vp, i32, i64, i64, i32, vp, i32, vp]
+        L.orc_select.argtypes = [vp, i64, i64, i64, i64, i32, vp, vp]
+        L.orc_groups_update.argtypes = [i64, i64, i64, i32, i32, vp, i32, i64, i64, i64, i32,
+                                        vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
+        L.orc_num_threads.argtypes = []
+        for f in (L.orc_score, L.orc_select, L.orc_groups_update, L.orc_num_threads):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise OracleError("%s failed with code %d" % (what, rc))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dt(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return DT_F32
+    if x.dtype == np.uint16:
+        return DT_BF16
+    raise TypeError("keys must be float32 or bf16 bits (uint16), got %s" % x.dtype)
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+def score(k: np.ndarray, mode: str = "l2", f: Optional[np.ndarray] = None, sign: int = 1) -> np.ndarray:
+    """Scores [n] float32 of rows k [n, D] (float32 or bf16 bits)."""
+    k = np.ascontiguousarray(k)
+    n, D = k.shape
+    out = np.empty(n, dtype=np.float32)
+    ff = None if f is None else np.ascontiguousarray(f, dtype=np.float32)
+    _check(lib().orc_score(_ptr(k), _dt(k), n, D, MODE_L2 if mode == "l2" else MODE_PROJ,
+                           _ptr(ff), sign, _ptr(out)), "orc_score")
+    return out
+
+
+def select(s: np.ndarray, budget: int, n_sink: int, recent: int, keep: str) -> np.ndarray:
+    """Kept row indices (ascending, int64) of the concatenated scores s."""
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    out = np.empty(max(1, s.size), dtype=np.int64)
+    n_out = ctypes.c_int64(0)
+    _check(lib().orc_select(_ptr(s), s.size, budget, n_sink, recent, 1 if keep == "low" else 0,
+                            _ptr(out), ctypes.byref(n_out)), "orc_select")
+    return out[:n_out.value].copy()
+
+
+class OracleCache:
+    """State of G independent groups (the kept rows of each), absorbing blocks.
+
+    Arrays: ``k``/``v`` [G, budget, D] (float32 or uint16 bf16 bits), ``s`` [G, budget]
+    float32 stored scores, ``pos`` [G, budget] int32, ``n`` [G] kept counts,
+    ``tokens`` [G] tokens seen (the true offset)."""
+
+    def __init__(self, G: int, D: int, dtype: str, budget: int, n_sink: int, recent: int,
+                 keep: str, mode: str = "l2", filters: Optional[np.ndarray] = None, sign: int = 1):
+        self.G, self.D, self.dtype = G, D, dtype
+        self.budget, self.n_sink, self.recent, self.keep = budget, n_sink, recent, keep
+        self.mode, self.sign = mode, sign
+        npdt = np.float32 if dtype == "f32" else np.uint16
+        self.k = np.zeros((G, budget, D), dtype=npdt)
+        self.v = np.zeros((G, budget, D), dtype=npdt)
+        self.s = np.zeros((G, budget), dtype=np.float32)
+        self.pos = np.zeros((G, budget), dtype=np.int32)
+        self.n = np.zeros(G, dtype=np.int64)
+        self.tokens = np.zeros(G, dtype=np.int64)
+        self.filters = None if filters is None else np.ascontiguousarray(
+            np.asarray(filters, dtype=np.float32).reshape(G, D))
+
+    def update(self, k_new: np.ndarray, v_new: np.ndarray, scores_in: Optional[np.ndarray] = None):
+        k_new = np.ascontiguousarray(k_new)
+        v_new = np.ascontiguousarray(v_new)
+        G, S, D = k_new.shape
+        assert G == self.G and D == self.D and v_new.shape == k_new.shape
+        assert k_new.dtype == self.k.dtype and v_new.dtype == self.k.dtype
+        if self.mode == "proj" and self.filters is None:
+            raise OracleError("projection mode needs filters")
+        si = None if scores_in is None else np.ascontiguousarray(scores_in, dtype=np.float32).reshape(G, S)
+        _check(lib().orc_groups_update(
+            G, self.budget, D, DT_F32 if self.dtype == "f32" else DT_BF16,
+            MODE_L2 if self.mode == "l2" else MODE_PROJ, _ptr(self.filters), self.sign,
+            self.budget, self.n_sink, self.recent, 1 if self.keep == "low" else 0,
+            _ptr(self.k), _ptr(self.v), _ptr(self.s), _ptr(self.pos), _ptr(self.n),
+            _ptr(self.tokens), _ptr(k_new), _ptr(v_new), S, _ptr(si)), "orc_groups_update")
+
+    def kept(self, g: int):
+        n = int(self.n[g])
+        return self.k[g, :n], self.v[g, :n], self.s[g, :n], self.pos[g, :n]
+
+    def copy(self) -> "OracleCache":
+        c = OracleCache.__new__(OracleCache)
+        c.__dict__.update({k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in self.__dict__.items()})
+        return c
