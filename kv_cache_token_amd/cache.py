@@ -1,0 +1,151 @@
+"""EvictingCache: the per-model bounded KV cache driven by the C ABI.
+
+It owns the device buffers (two cache buffer sets used alternately when a block
+evicts, a keep-index buffer and the incoming-score buffer), the kept-row count
+and the true offset (tokens seen, Q-Filters page, "RoPE positions had to be
+fixed first").  Each ``update`` is the query-free step of the pages
+(Q-Filters page and L2Norm page, "How it works"): score the incoming rows,
+select, compact; all arithmetic runs in the library's kernels on one stream.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import api
+
+D = api.D
+
+
+class EvictingCache:
+    def __init__(self, L: int, B: int, H: int, budget: int, n_sink: int = 4, recent: int = 0,
+                 keep: str = "low", mode: str = "l2", filters=None, sign: int = 1, dtype: str = "bf16",
+                 device="cuda", calib_tokens: int = 0, stream=None):
+        import torch
+        self.L, self.B, self.H, self.G = L, B, H, L * B * H
+        self.budget, self.n_sink, self.recent = budget, n_sink, recent
+        self.mode, self.sign = mode, sign
+        self.keep = "high" if mode == "proj" else keep
+        self.shape = api.make_shape(L, B, H, dtype)
+        self.params = api.make_params(budget, n_sink, recent, self.keep)
+        self.calib_tokens = calib_tokens
+        self.stream = stream
+        self.device = torch.device(device)
+        if mode not in ("l2", "proj"):
+            raise ValueError("mode must be 'l2' or 'proj'")
+        if mode == "proj" and filters is None and calib_tokens <= 0:
+            raise ValueError("projection needs filters or calib_tokens > 0 (key-SVD fallback)")
+        if n_sink + recent >= budget:
+            raise ValueError("n_sink + recent must be below budget")
+        if mode == "proj" and sign not in (1, -1):
+            raise ValueError("sign must be +1 or -1")
+        td = api.torch_dtype(self.shape.dtype)
+        G = self.G
+
+        def bufset():
+            return (torch.empty((G, budget, D), dtype=td, device=self.device),
+                    torch.empty((G, budget, D), dtype=td, device=self.device),
+                    torch.empty((G, budget), dtype=torch.float32, device=self.device),
+                    torch.empty((G, budget), dtype=torch.int32, device=self.device))
+
+        self._bufs = [bufset(), bufset()]
+        self._cur = 0
+        self.keep_idx = torch.empty((G, budget), dtype=torch.int32, device=self.device)
+        self._s_new = torch.empty((G, 1), dtype=torch.float32, device=self.device)
+        self.score_shape = self.shape
+        self.filters = None
+        if filters is not None:
+            self.set_filters(filters)
+        self.n_kept = 0
+        self.tokens_seen = 0
+
+    # -- filters -----------------------------------------------------------
+    def set_filters(self, filters, per_group: bool = False) -> None:
+        """Freeze the projection filters: [L, H, D] (per layer and KV head) or,
+        with per_group, [G, D] (one per (layer, batch, head) group)."""
+        import torch
+        f = torch.as_tensor(np.asarray(filters, dtype=np.float32) if not isinstance(filters, torch.Tensor)
+                            else filters, dtype=torch.float32)
+        if per_group:
+            f = f.reshape(self.L * self.B, self.H, D)
+            self.score_shape = api.make_shape(self.L * self.B, 1, self.H, self.shape.dtype)
+        else:
+            f = f.reshape(self.L, self.H, D)
+            self.score_shape = self.shape
+        self.filters = f.to(self.device).contiguous()
+
+    def _freeze_fallback(self, k_new) -> None:
+        S = k_new.shape[1]
+        if self.tokens_seen != 0 or S < self.calib_tokens:
+            raise NotImplementedError("key-SVD fallback: the first block must hold at least calib_tokens "
+                                      "rows (the pre-calibration passthrough is not implemented)")
+        import torch
+        first = k_new[:, :self.calib_tokens].contiguous().cpu()
+        if first.dtype == torch.bfloat16:
+            host = first.view(torch.int16).numpy().view(np.uint16)
+        else:
+            host = first.numpy()
+        self.set_filters(api.qf_filters_from_keys(host, self.calib_tokens), per_group=True)
+
+    # -- state -------------------------------------------------------------
+    @property
+    def offset(self) -> int:
+        """Absolute tokens absorbed (the position the next token will get)."""
+        return self.tokens_seen
+
+    def buffers(self):
+        return self._bufs[self._cur]
+
+    def kept(self):
+        k, v, s, p = self._bufs[self._cur]
+        n = self.n_kept
+        return k[:, :n], v[:, :n], s[:, :n], p[:, :n]
+
+    def last_scores(self):
+        """Scores [G, S] the last update computed for its incoming rows."""
+        return self._s_new
+
+    def reset(self) -> None:
+        self.n_kept = 0
+        self.tokens_seen = 0
+        if self.mode == "proj" and self.calib_tokens > 0 and self.score_shape is not self.shape:
+            self.filters = None
+
+    def stats(self) -> dict:
+        return api.kvx_stats(self.shape, self.tokens_seen, self.n_kept, self.mode)
+
+    # -- the step ----------------------------------------------------------
+    def _scores(self, S: int):
+        import torch
+        if self._s_new.shape[1] != S:
+            self._s_new = torch.empty((self.G, max(S, 1)), dtype=torch.float32, device=self.device)
+        return self._s_new
+
+    def update(self, k_new, v_new) -> None:
+        """Absorb one block: k_new, v_new [G, S, D] (or [L, B, H, S, D]) contiguous."""
+        S = k_new.shape[-2]
+        k_new = k_new.reshape(self.G, S, D)
+        v_new = v_new.reshape(self.G, S, D)
+        if S == 0:
+            return
+        if self.mode == "proj" and self.filters is None:
+            self._freeze_fallback(k_new)
+        s_new = self._scores(S)
+        api.qf_score_keys(k_new, self.score_shape, S, self.mode, self.filters, self.sign, s_new, self.stream)
+        k, v, s, p = self._bufs[self._cur]
+        nk, pos_base = self.n_kept, self.tokens_seen
+        if S == 1:
+            api.kv_evict_one_inplace(k, v, s, p, k_new, v_new, s_new, pos_base, self.shape, nk, self.params,
+                                     self.stream)
+        elif nk + S <= self.budget:
+            api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, None, self.shape, nk, S,
+                                  self.params, k, v, s, p, self.stream)
+        else:
+            api.kv_evict_topk(s, s_new, self.shape, nk, S, self.params, self.keep_idx, None, self.stream)
+            ko, vo, so, po = self._bufs[1 - self._cur]
+            api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, self.keep_idx, self.shape, nk, S,
+                                  self.params, ko, vo, so, po, self.stream)
+            self._cur = 1 - self._cur
+        self.n_kept = min(nk + S, self.budget)
+        self.tokens_seen += S

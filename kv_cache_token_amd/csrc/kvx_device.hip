@@ -1,0 +1,666 @@
+// Device half of libkvevict: the HIP kernels of the eviction step for gfx950 and
+// the C-ABI entry points that validate and launch them.
+//
+// Pages: "Q-Filters — Query-Agnostic Projection Eviction" ("How it works",
+// "Metal kernels", "Adaptation notes") and "L2Norm — Intrinsic Key-Norm
+// Eviction" ("How it works").  The Metal design on the first page rescored all
+// rows, sorted on the host side to find the keep threshold and compacted with
+// one threadgroup per group; here only incoming rows are scored, the threshold
+// is found by an on-chip radix select, and the copy runs as a separate
+// bandwidth-shaped kernel over all groups at once.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvevict.h"
+#include "kvx_common.h"
+
+namespace kvx {
+namespace {
+
+constexpr int kD = KVX_HEAD_DIM;
+
+template <int DT>
+struct Row {
+    static constexpr int kElemBytes = DT == KVX_BF16 ? 2 : 4;
+    static constexpr int kBytes = kD * kElemBytes;   // 256 (bf16) or 512 (fp32)
+    static constexpr int kLanes = kBytes / 16;        // lanes covering one row, 16 B each
+    static constexpr int kElemsPerLane = 16 / kElemBytes;
+};
+
+__device__ __forceinline__ uint4 ld16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(char *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+// Widen the 16 bytes a lane holds to float32 (exact for both element types).
+template <int DT>
+__device__ __forceinline__ void widen(uint4 r, float *x) {
+    if constexpr (DT == KVX_BF16) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);           // element 2i   (low half)
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);  // element 2i+1 (high half)
+        }
+    } else {
+        x[0] = __uint_as_float(r.x);
+        x[1] = __uint_as_float(r.y);
+        x[2] = __uint_as_float(r.z);
+        x[3] = __uint_as_float(r.w);
+    }
+}
+
+// Order-preserving map of a score to an unsigned key, "higher key = better".
+// keep_low ranks by -s.  -0 becomes +0 first so that the two tie.
+__device__ __forceinline__ uint32_t select_key(float s, int keep_low) {
+    float c = keep_low ? -s : s;
+    c = c + 0.0f;
+    const uint32_t b = __float_as_uint(c);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// Step 1: score kernel.  Kernel rows are [n_rows, D] contiguous (n_rows = G*S).
+// A row is read by kLanes lanes, 16 bytes each (bf16: 16 lanes, 4 rows per
+// wave per load).  Each lane sums its elements in order with fused
+// multiply-adds, then the row's lanes combine by an xor butterfly; the order is
+// a function of the row alone, so a row's score does not depend on S, on the
+// tile it falls in or on the grid.
+// ---------------------------------------------------------------------------
+template <int DT, int MODE, int U>
+__global__ __launch_bounds__(256) void score_kernel(const char *__restrict__ k, uint32_t n_rows,
+                                                    uint32_t S, uint32_t BH, uint32_t H,
+                                                    const float *__restrict__ filt, float sign,
+                                                    float *__restrict__ out) {
+    using R = Row<DT>;
+    constexpr int kRowsPerLoad = 64 / R::kLanes;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t sub = lane / R::kLanes;
+    const uint32_t part = lane % R::kLanes;
+    const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const uint32_t row0 = wave * (kRowsPerLoad * U);
+
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t r = row0 + u * kRowsPerLoad + sub;
+        raw[u] = r < n_rows ? ld16(k + (size_t)r * R::kBytes + part * 16) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t r = row0 + u * kRowsPerLoad + sub;
+        float x[R::kElemsPerLane];
+        widen<DT>(raw[u], x);
+        float acc = 0.0f;
+        if constexpr (MODE == KVX_SCORE_L2) {
+#pragma unroll
+            for (int e = 0; e < R::kElemsPerLane; ++e) acc = __builtin_fmaf(x[e], x[e], acc);
+        } else {
+            const uint32_t g = r < n_rows ? r / S : 0u;
+            const uint32_t l = g / BH, h = g % H;
+            const float4 *f4 = reinterpret_cast<const float4 *>(
+                filt + (size_t)(l * H + h) * kD + part * R::kElemsPerLane);
+            float f[R::kElemsPerLane];
+#pragma unroll
+            for (int q = 0; q < R::kElemsPerLane / 4; ++q) {
+                const float4 v = f4[q];
+                f[4 * q] = v.x;
+                f[4 * q + 1] = v.y;
+                f[4 * q + 2] = v.z;
+                f[4 * q + 3] = v.w;
+            }
+#pragma unroll
+            for (int e = 0; e < R::kElemsPerLane; ++e) acc = __builtin_fmaf(x[e], f[e], acc);
+        }
+#pragma unroll
+        for (int off = R::kLanes / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+        if (part == 0 && r < n_rows) {
+            const float s = MODE == KVX_SCORE_L2 ? __builtin_sqrtf(acc) : sign * acc;
+            out[r] = s + 0.0f;  // -0 -> +0
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Steps 2-3: selection.  One 1024-thread workgroup per group.  Thread t holds
+// the keys of rows t, t + 1024, ... (M of them) in registers, so every load is
+// coalesced.  The budget-th largest key tau is found with four 8-bit radix
+// passes over an LDS histogram; then the kept rows are those with key > tau
+// plus the first `quota` rows (in row order) with key == tau, and their
+// indices are written in row order using per-64-row chunk counts.
+// Protected rows get key 0xFFFFFFFF, above every real score's key.
+// ---------------------------------------------------------------------------
+template <int M>
+__global__ __launch_bounds__(1024) void select_kernel(const float *__restrict__ s_kept,
+                                                      const float *__restrict__ s_new, int n_kept,
+                                                      int S, int budget, int n_sink, int recent,
+                                                      int keep_low, int32_t *__restrict__ keep_idx) {
+    const int g = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int n_total = n_kept + S;
+    int32_t *out = keep_idx + (size_t)g * budget;
+    if (n_total <= budget) {
+        for (int r = t; r < n_total; r += 1024) out[r] = r;
+        return;
+    }
+    const float *sk = s_kept + (size_t)g * budget;
+    const float *sn = s_new + (size_t)g * S;
+
+    uint32_t key[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int r = i * 1024 + t;
+        uint32_t kk = 0;
+        if (r < n_total) {
+            const float s = r < n_kept ? sk[r] : sn[r - n_kept];
+            const bool prot = r < n_sink || r >= n_total - recent;
+            kk = prot ? 0xFFFFFFFFu : select_key(s, keep_low);
+        }
+        key[i] = kk;
+    }
+
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t sel[2];
+    __shared__ uint32_t chunk[KVX_MAX_TOTAL / 64];
+
+    uint32_t prefix = 0, pmask = 0, krem = (uint32_t)budget;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        if (t < 256) hist[t] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            const int r = i * 1024 + t;
+            bool act = r < n_total && (key[i] & pmask) == prefix;
+            const uint32_t d = (key[i] >> shift) & 0xFFu;
+            // A few rounds of wave-aggregated increments take the common digits
+            // (scores cluster, so one digit often covers most of a wave).
+            for (int it = 0; it < 4; ++it) {
+                const uint64_t am = __ballot(act);
+                if (am == 0) break;
+                const int leader = __ffsll((unsigned long long)am) - 1;
+                const uint32_t ld = __shfl(d, leader);
+                const bool mine = act && d == ld;
+                const uint64_t m = __ballot(mine);
+                if (lane == leader) atomicAdd(&hist[ld], (uint32_t)__popcll(m));
+                if (mine) act = false;
+            }
+            if (act) atomicAdd(&hist[d], 1u);
+        }
+        __syncthreads();
+        if (w == 0) {
+            const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1];
+            const uint32_t c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+            const uint32_t local = c0 + c1 + c2 + c3;
+            uint32_t incl = local;  // keys in this lane's bins or any higher bin
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t v = __shfl_down(incl, off);
+                if (lane + off < 64) incl += v;
+            }
+            const uint32_t above = incl - local;
+            if (above < krem && krem <= incl) {
+                uint32_t cum = above, d, nk;
+                if (cum + c3 >= krem) {
+                    d = 4 * lane + 3;
+                    nk = krem - cum;
+                } else if ((cum += c3) + c2 >= krem) {
+                    d = 4 * lane + 2;
+                    nk = krem - cum;
+                } else if ((cum += c2) + c1 >= krem) {
+                    d = 4 * lane + 1;
+                    nk = krem - cum;
+                } else {
+                    cum += c1;
+                    d = 4 * lane;
+                    nk = krem - cum;
+                }
+                sel[0] = d;
+                sel[1] = nk;
+            }
+        }
+        __syncthreads();
+        prefix |= sel[0] << shift;
+        pmask |= 0xFFu << shift;
+        krem = sel[1];
+    }
+    const uint32_t tau = prefix, quota = krem;
+
+    // Per-chunk (64 consecutive rows) counts of key > tau and key == tau,
+    // packed as (gt << 16) | eq; both stay below 2^16.
+    const int nchunks = (n_total + 63) >> 6;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int c = i * 16 + w;
+        const int r = c * 64 + lane;
+        const bool valid = r < n_total;
+        const uint64_t gm = __ballot(valid && key[i] > tau);
+        const uint64_t em = __ballot(valid && key[i] == tau);
+        if (lane == 0 && c < nchunks)
+            chunk[c] = ((uint32_t)__popcll(gm) << 16) | (uint32_t)__popcll(em);
+    }
+    __syncthreads();
+    if (w == 0) {
+        uint32_t a[4], local = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * lane + j;
+            a[j] = c < nchunks ? chunk[c] : 0u;
+            local += a[j];
+        }
+        uint32_t incl = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        uint32_t run = incl - local;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * lane + j;
+            if (c < nchunks) chunk[c] = run;
+            run += a[j];
+        }
+    }
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int c = i * 16 + w;
+        const int r = c * 64 + lane;
+        const bool valid = r < n_total;
+        const uint64_t gm = __ballot(valid && key[i] > tau);
+        const uint64_t em = __ballot(valid && key[i] == tau);
+        if (valid) {
+            const uint32_t base = chunk[c];
+            const uint32_t gb = (base >> 16) + (uint32_t)__popcll(gm & below);
+            const uint32_t eb = (base & 0xFFFFu) + (uint32_t)__popcll(em & below);
+            // Exactly `budget` rows qualify, so every slot is below budget; the
+            // bound check only keeps a corrupt input from writing past the row.
+            uint32_t slot = 0xFFFFFFFFu;
+            if (key[i] > tau)
+                slot = gb + min(eb, quota);
+            else if (key[i] == tau && eb < quota)
+                slot = gb + eb;
+            if (slot < (uint32_t)budget) out[slot] = r;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Step 4: gather.  Output rows j in [j0, n_out) of every group; blocks are
+// numbered group-major.  Each row is kLanes lanes x 16 B for K and the same for
+// V; the lane with part == 0 also moves the score and the position.
+// keep_idx == nullptr means the identity (nothing evicted).
+// ---------------------------------------------------------------------------
+template <int DT, int U>
+__global__ __launch_bounds__(256) void gather_kernel(
+    const char *__restrict__ k_kept, const char *__restrict__ v_kept,
+    const float *__restrict__ s_kept, const int32_t *__restrict__ pos_kept,
+    const char *__restrict__ k_new, const char *__restrict__ v_new,
+    const float *__restrict__ s_new, int32_t pos_base, const int32_t *__restrict__ keep_idx,
+    int n_kept, int S, int budget, int j0, int n_out, int blocks_per_group, char *__restrict__ k_out,
+    char *__restrict__ v_out, float *__restrict__ s_out, int32_t *__restrict__ pos_out) {
+    using R = Row<DT>;
+    constexpr int kRowsPerPass = 256 / R::kLanes;
+    const int g = blockIdx.x / blocks_per_group;
+    const int b = blockIdx.x - g * blocks_per_group;
+    const int part = threadIdx.x % R::kLanes;
+    const int sub = threadIdx.x / R::kLanes;
+    const int jb = j0 + b * (kRowsPerPass * U);
+    const size_t cache_row0 = (size_t)g * budget;
+    const size_t new_row0 = (size_t)g * S;
+
+    uint4 kr[U], vr[U];
+    int src[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = jb + u * kRowsPerPass + sub;
+        src[u] = -1;
+        if (j < n_out) {
+            int r = keep_idx ? keep_idx[cache_row0 + j] : j;
+            if ((unsigned)r >= (unsigned)(n_kept + S)) r = 0;  // keep a corrupt index in bounds
+            src[u] = r;
+            const size_t off = r < n_kept ? (cache_row0 + r) * R::kBytes
+                                          : (new_row0 + (r - n_kept)) * R::kBytes;
+            const char *kb = r < n_kept ? k_kept : k_new;
+            const char *vb = r < n_kept ? v_kept : v_new;
+            kr[u] = ld16(kb + off + part * 16);
+            vr[u] = ld16(vb + off + part * 16);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = jb + u * kRowsPerPass + sub;
+        if (j < n_out) {
+            const size_t off = (cache_row0 + j) * R::kBytes + part * 16;
+            st16(k_out + off, kr[u]);
+            st16(v_out + off, vr[u]);
+            if (part == 0) {
+                const int r = src[u];
+                s_out[cache_row0 + j] = r < n_kept ? s_kept[cache_row0 + r] : s_new[new_row0 + (r - n_kept)];
+                pos_out[cache_row0 + j] = r < n_kept ? pos_kept[cache_row0 + r] : pos_base + (r - n_kept);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: one incoming row per group, in place.  One 256-thread workgroup per
+// group.  The victim is the candidate with the smallest key, the higher row on
+// equal keys (the last row in the general (key desc, row asc) order).  Rows
+// after it move down one row in chunks of C rows: every thread loads its part
+// of the chunk, waits for its loads to land, the workgroup meets at a barrier,
+// then the chunk is stored one row lower.  A chunk only writes rows below the
+// next chunk's sources, so chunk-by-chunk order makes the shift race-free.
+// ---------------------------------------------------------------------------
+template <int DT, int U>
+__global__ __launch_bounds__(256) void evict_one_kernel(
+    char *__restrict__ k_cache, char *__restrict__ v_cache, float *__restrict__ s_cache,
+    int32_t *__restrict__ pos_cache, const char *__restrict__ k_new, const char *__restrict__ v_new,
+    const float *__restrict__ s_new, int32_t pos_base, int n_kept, int budget, int n_sink,
+    int recent, int keep_low) {
+    using R = Row<DT>;
+    constexpr int kSlots = 2 * R::kLanes;          // K lanes then V lanes of one row
+    constexpr int kRowsPerPass = 256 / kSlots;
+    constexpr int C = kRowsPerPass * U;            // rows per chunk (<= 256)
+    const int g = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    char *kc = k_cache + (size_t)g * budget * R::kBytes;
+    char *vc = v_cache + (size_t)g * budget * R::kBytes;
+    float *sc = s_cache + (size_t)g * budget;
+    int32_t *pc = pos_cache + (size_t)g * budget;
+
+    int dst_new = n_kept;
+    if (n_kept >= budget) {
+        const int n_total = budget + 1;
+        const int lo = n_sink, hi = n_total - recent;
+        uint64_t best = ~0ull;
+        for (int r = lo + t; r < hi; r += 256) {
+            const float s = r < budget ? sc[r] : s_new[g];
+            const uint64_t kk = ((uint64_t)select_key(s, keep_low) << 32) |
+                                (uint64_t)(0xFFFFFFFFu - (uint32_t)r);
+            best = kk < best ? kk : best;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const uint32_t lo32 = __shfl_xor((uint32_t)best, off);
+            const uint32_t hi32 = __shfl_xor((uint32_t)(best >> 32), off);
+            const uint64_t o = ((uint64_t)hi32 << 32) | lo32;
+            best = o < best ? o : best;
+        }
+        __shared__ uint64_t wbest[4];
+        if (lane == 0) wbest[w] = best;
+        __syncthreads();
+        best = wbest[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) best = wbest[i] < best ? wbest[i] : best;
+        const int victim = (int)(0xFFFFFFFFu - (uint32_t)best);
+        if (victim >= budget) return;  // the incoming row is the one dropped
+
+        const int slot = t % kSlots;
+        const int half = slot / R::kLanes;  // 0: K, 1: V
+        const int part = slot % R::kLanes;
+        const int sub = t / kSlots;
+        char *base = half ? vc : kc;
+        for (int c0 = victim + 1; c0 < budget; c0 += C) {
+            uint4 d[U];
+            float sv = 0.0f;
+            int32_t pv = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int src = c0 + u * kRowsPerPass + sub;
+                if (src < budget) d[u] = ld16(base + (size_t)src * R::kBytes + part * 16);
+            }
+            if (t < C && c0 + t < budget) {
+                sv = sc[c0 + t];
+                pv = pc[c0 + t];
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int src = c0 + u * kRowsPerPass + sub;
+                if (src < budget) st16(base + (size_t)(src - 1) * R::kBytes + part * 16, d[u]);
+            }
+            if (t < C && c0 + t < budget) {
+                sc[c0 + t - 1] = sv;
+                pc[c0 + t - 1] = pv;
+            }
+        }
+        dst_new = budget - 1;
+    }
+    if (t < kSlots) {
+        const int half = t / R::kLanes, part = t % R::kLanes;
+        const char *src = (half ? v_new : k_new) + (size_t)g * R::kBytes + part * 16;
+        char *dst = (half ? vc : kc) + (size_t)dst_new * R::kBytes + part * 16;
+        st16(dst, ld16(src));
+    }
+    if (t == 0) {
+        sc[dst_new] = s_new[g];
+        pc[dst_new] = pos_base;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side validation shared by the entry points.
+// ---------------------------------------------------------------------------
+int check_shape(const kvx_shape &sh, int64_t *G) {
+    if (sh.L < 0 || sh.B < 0 || sh.H < 0)
+        return set_error(KVX_EINVAL, "shape: L, B, H must be >= 0 (got %lld, %lld, %lld)",
+                         (long long)sh.L, (long long)sh.B, (long long)sh.H);
+    if (sh.D != kD) return set_error(KVX_EINVAL, "shape: D must be %d (got %lld)", kD, (long long)sh.D);
+    if (sh.dtype != KVX_BF16 && sh.dtype != KVX_F32)
+        return set_error(KVX_EINVAL, "shape: dtype must be KVX_BF16 or KVX_F32 (got %d)", (int)sh.dtype);
+    if (sh.L > INT32_MAX || sh.B > INT32_MAX || sh.H > INT32_MAX ||
+        (sh.L > 0 && sh.B > 0 && sh.H > 0 && sh.L * sh.B > INT32_MAX / sh.H))
+        return set_error(KVX_ERANGE, "shape: L*B*H must be below 2^31");
+    *G = sh.L * sh.B * sh.H;
+    return KVX_OK;
+}
+
+int check_params(const kvx_evict_params &p) {
+    if (p.budget < 1) return set_error(KVX_EINVAL, "params: budget must be >= 1 (got %lld)", (long long)p.budget);
+    if (p.n_sink < 0 || p.recent < 0)
+        return set_error(KVX_EINVAL, "params: n_sink and recent must be >= 0");
+    if (p.n_sink + p.recent >= p.budget)
+        return set_error(KVX_EINVAL, "params: n_sink + recent (%lld) must be below budget (%lld)",
+                         (long long)(p.n_sink + p.recent), (long long)p.budget);
+    if (p.keep != KVX_KEEP_HIGH && p.keep != KVX_KEEP_LOW)
+        return set_error(KVX_EINVAL, "params: keep must be KVX_KEEP_HIGH or KVX_KEEP_LOW (got %d)", (int)p.keep);
+    if (p.budget > KVX_MAX_BUDGET)
+        return set_error(KVX_ERANGE, "params: budget %lld exceeds KVX_MAX_BUDGET (%d)",
+                         (long long)p.budget, KVX_MAX_BUDGET);
+    return KVX_OK;
+}
+
+int check_launch(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return set_error(KVX_EDEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return KVX_OK;
+}
+
+int validate_select_sizes(const kvx_shape &shape, int64_t n_kept, int64_t S, const kvx_evict_params &p,
+                          int64_t *G) {
+    int rc = check_shape(shape, G);
+    if (rc) return rc;
+    if ((rc = check_params(p))) return rc;
+    if (S < 0) return set_error(KVX_EINVAL, "S must be >= 0 (got %lld)", (long long)S);
+    if (n_kept < 0 || n_kept > p.budget)
+        return set_error(KVX_EINVAL, "n_kept must be in [0, budget] (got %lld, budget %lld)",
+                         (long long)n_kept, (long long)p.budget);
+    if (n_kept + S > KVX_MAX_TOTAL)
+        return set_error(KVX_ERANGE, "n_kept + S = %lld exceeds KVX_MAX_TOTAL (%d)",
+                         (long long)(n_kept + S), KVX_MAX_TOTAL);
+    return KVX_OK;
+}
+
+template <int DT>
+int launch_score(const void *k_new, int64_t G, const kvx_shape &sh, int64_t S, int32_t mode,
+                 const float *filters, int32_t sign, float *s_new, hipStream_t st) {
+    constexpr int U = 4;
+    constexpr int kRowsPerBlock = 4 * (64 / Row<DT>::kLanes) * U;
+    const uint32_t n_rows = (uint32_t)(G * S);
+    const uint32_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    const uint32_t BH = (uint32_t)(sh.B * sh.H), H = (uint32_t)sh.H;
+    if (mode == KVX_SCORE_L2)
+        score_kernel<DT, KVX_SCORE_L2, U><<<blocks, 256, 0, st>>>(
+            (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, 1.0f, s_new);
+    else
+        score_kernel<DT, KVX_SCORE_PROJ, U><<<blocks, 256, 0, st>>>(
+            (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, (float)sign, s_new);
+    return check_launch("qf_score_keys");
+}
+
+template <int DT>
+int launch_gather(const void *k_kept, const void *v_kept, const float *s_kept, const int32_t *pos_kept,
+                  const void *k_new, const void *v_new, const float *s_new, int32_t pos_base,
+                  const int32_t *keep_idx, int64_t G, int n_kept, int S, int budget, int j0, int n_out,
+                  void *k_out, void *v_out, float *s_out, int32_t *pos_out, hipStream_t st) {
+    constexpr int U = 4;
+    constexpr int kRowsPerBlock = (256 / Row<DT>::kLanes) * U;
+    const int rows = n_out - j0;
+    if (rows <= 0 || G == 0) return KVX_OK;
+    const int bpg = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int64_t blocks = G * bpg;
+    if (blocks > INT32_MAX) return set_error(KVX_ERANGE, "kv_compact_gather: grid too large");
+    gather_kernel<DT, U><<<(uint32_t)blocks, 256, 0, st>>>(
+        (const char *)k_kept, (const char *)v_kept, s_kept, pos_kept, (const char *)k_new,
+        (const char *)v_new, s_new, pos_base, keep_idx, n_kept, S, budget, j0, n_out, bpg,
+        (char *)k_out, (char *)v_out, s_out, pos_out);
+    return check_launch("kv_compact_gather");
+}
+
+}  // namespace
+}  // namespace kvx
+
+using namespace kvx;
+
+extern "C" {
+
+KVX_API int qf_score_keys(const void *k_new, kvx_shape shape, int64_t S, int32_t mode,
+                          const float *filters, int32_t sign, float *s_new, void *stream) {
+    clear_error();
+    int64_t G = 0;
+    int rc = check_shape(shape, &G);
+    if (rc) return rc;
+    if (S < 0) return set_error(KVX_EINVAL, "qf_score_keys: S must be >= 0");
+    if (mode != KVX_SCORE_L2 && mode != KVX_SCORE_PROJ)
+        return set_error(KVX_EINVAL, "qf_score_keys: mode must be KVX_SCORE_L2 or KVX_SCORE_PROJ (got %d)", (int)mode);
+    if (mode == KVX_SCORE_PROJ && sign != 1 && sign != -1)
+        return set_error(KVX_EINVAL, "qf_score_keys: sign must be +1 or -1 (got %d)", (int)sign);
+    if (mode == KVX_SCORE_PROJ && filters == nullptr)
+        return set_error(KVX_EINVAL, "qf_score_keys: projection needs filters");
+    if (G == 0 || S == 0) return KVX_OK;
+    if (G * S >= ((int64_t)1 << 31)) return set_error(KVX_ERANGE, "qf_score_keys: G*S must be below 2^31");
+    if (!k_new || !s_new) return set_error(KVX_EINVAL, "qf_score_keys: NULL buffer");
+    hipStream_t st = (hipStream_t)stream;
+    return shape.dtype == KVX_BF16 ? launch_score<KVX_BF16>(k_new, G, shape, S, mode, filters, sign, s_new, st)
+                                   : launch_score<KVX_F32>(k_new, G, shape, S, mode, filters, sign, s_new, st);
+}
+
+KVX_API int kv_evict_workspace_size(kvx_shape shape, int64_t n_kept, int64_t S, kvx_evict_params p,
+                                    size_t *bytes) {
+    clear_error();
+    int64_t G = 0;
+    int rc = validate_select_sizes(shape, n_kept, S, p, &G);
+    if (rc) return rc;
+    if (!bytes) return set_error(KVX_EINVAL, "kv_evict_workspace_size: NULL output");
+    *bytes = 0;
+    return KVX_OK;
+}
+
+KVX_API int kv_evict_topk(const float *s_kept, const float *s_new, kvx_shape shape, int64_t n_kept,
+                          int64_t S, kvx_evict_params p, int32_t *keep_idx, void *ws, size_t ws_bytes,
+                          void *stream) {
+    clear_error();
+    (void)ws;
+    (void)ws_bytes;
+    int64_t G = 0;
+    int rc = validate_select_sizes(shape, n_kept, S, p, &G);
+    if (rc) return rc;
+    const int64_t n_total = n_kept + S;
+    if (G == 0 || n_total == 0) return KVX_OK;
+    if (!keep_idx || (n_kept > 0 && !s_kept) || (S > 0 && !s_new))
+        return set_error(KVX_EINVAL, "kv_evict_topk: NULL buffer");
+    hipStream_t st = (hipStream_t)stream;
+    const int a = (int)n_kept, b = (int)S, bud = (int)p.budget, ns = (int)p.n_sink, rc2 = (int)p.recent;
+    const int kl = p.keep == KVX_KEEP_LOW;
+    const uint32_t grid = (uint32_t)G;
+    if (n_total <= 1024)
+        select_kernel<1><<<grid, 1024, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    else if (n_total <= 2048)
+        select_kernel<2><<<grid, 1024, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    else if (n_total <= 4096)
+        select_kernel<4><<<grid, 1024, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    else if (n_total <= 8192)
+        select_kernel<8><<<grid, 1024, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    else
+        select_kernel<16><<<grid, 1024, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    return check_launch("kv_evict_topk");
+}
+
+KVX_API int kv_compact_gather(const void *k_kept, const void *v_kept, const float *s_kept,
+                              const int32_t *pos_kept, const void *k_new, const void *v_new,
+                              const float *s_new, int64_t pos_base, const int32_t *keep_idx,
+                              kvx_shape shape, int64_t n_kept, int64_t S, kvx_evict_params p,
+                              void *k_out, void *v_out, float *s_out, int32_t *pos_out, void *stream) {
+    clear_error();
+    int64_t G = 0;
+    int rc = validate_select_sizes(shape, n_kept, S, p, &G);
+    if (rc) return rc;
+    const int64_t n_total = n_kept + S;
+    const bool evict = n_total > p.budget;
+    const int n_out = (int)(evict ? p.budget : n_total);
+    if (pos_base < 0 || pos_base + S > INT32_MAX)
+        return set_error(KVX_ERANGE, "kv_compact_gather: positions must fit int32 (pos_base %lld, S %lld)",
+                         (long long)pos_base, (long long)S);
+    if (G == 0 || n_out == 0) return KVX_OK;
+    if (!k_out || !v_out || !s_out || !pos_out) return set_error(KVX_EINVAL, "kv_compact_gather: NULL output");
+    if (n_kept > 0 && (!k_kept || !v_kept || !s_kept || !pos_kept))
+        return set_error(KVX_EINVAL, "kv_compact_gather: NULL kept buffer");
+    if (S > 0 && (!k_new || !v_new || !s_new)) return set_error(KVX_EINVAL, "kv_compact_gather: NULL incoming buffer");
+    if (evict && !keep_idx) return set_error(KVX_EINVAL, "kv_compact_gather: keep_idx is required when evicting");
+    const int n_alias = (k_out == k_kept) + (v_out == v_kept) + ((const void *)s_out == (const void *)s_kept) +
+                        ((const void *)pos_out == (const void *)pos_kept);
+    if (n_alias != 0 && n_alias != 4)
+        return set_error(KVX_EINVAL, "kv_compact_gather: outputs must alias all four kept buffers or none");
+    if (n_alias == 4 && evict)
+        return set_error(KVX_EINVAL, "kv_compact_gather: in-place compaction is only allowed without eviction");
+    const int j0 = n_alias == 4 ? (int)n_kept : 0;  // in place: only the incoming rows move
+    const int32_t *idx = evict ? keep_idx : nullptr;
+    hipStream_t st = (hipStream_t)stream;
+    if (shape.dtype == KVX_BF16)
+        return launch_gather<KVX_BF16>(k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, (int32_t)pos_base,
+                                       idx, G, (int)n_kept, (int)S, (int)p.budget, j0, n_out, k_out, v_out,
+                                       s_out, pos_out, st);
+    return launch_gather<KVX_F32>(k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, (int32_t)pos_base, idx,
+                                  G, (int)n_kept, (int)S, (int)p.budget, j0, n_out, k_out, v_out, s_out,
+                                  pos_out, st);
+}
+
+KVX_API int kv_evict_one_inplace(void *k_cache, void *v_cache, float *s_cache, int32_t *pos_cache,
+                                 const void *k_new, const void *v_new, const float *s_new, int64_t pos_base,
+                                 kvx_shape shape, int64_t n_kept, kvx_evict_params p, void *stream) {
+    clear_error();
+    int64_t G = 0;
+    int rc = validate_select_sizes(shape, n_kept, 1, p, &G);
+    if (rc) return rc;
+    if (pos_base < 0 || pos_base >= INT32_MAX)
+        return set_error(KVX_ERANGE, "kv_evict_one_inplace: position must fit int32");
+    if (G == 0) return KVX_OK;
+    if (!k_cache || !v_cache || !s_cache || !pos_cache || !k_new || !v_new || !s_new)
+        return set_error(KVX_EINVAL, "kv_evict_one_inplace: NULL buffer");
+    hipStream_t st = (hipStream_t)stream;
+    if (G > INT32_MAX) return set_error(KVX_ERANGE, "kv_evict_one_inplace: too many groups");
+    const int kl = p.keep == KVX_KEEP_LOW;
+    if (shape.dtype == KVX_BF16)
+        evict_one_kernel<KVX_BF16, 8><<<(uint32_t)G, 256, 0, st>>>(
+            (char *)k_cache, (char *)v_cache, s_cache, pos_cache, (const char *)k_new, (const char *)v_new, s_new,
+            (int32_t)pos_base, (int)n_kept, (int)p.budget, (int)p.n_sink, (int)p.recent, kl);
+    else
+        evict_one_kernel<KVX_F32, 8><<<(uint32_t)G, 256, 0, st>>>(
+            (char *)k_cache, (char *)v_cache, s_cache, pos_cache, (const char *)k_new, (const char *)v_new, s_new,
+            (int32_t)pos_base, (int)n_kept, (int)p.budget, (int)p.n_sink, (int)p.recent, kl);
+    return check_launch("kv_evict_one_inplace");
+}
+
+}  // extern "C"

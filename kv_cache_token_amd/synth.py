@@ -184,6 +184,11 @@ def group_stream(cfg: Config, g: int, n_chunks: Optional[int] = None) -> List[Tu
     return [group_chunk(cfg, g, c) for c in range(n)]
 
 
+def decode_block(cfg: Config, g: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The decode workload's 256 single-token steps of group g as one [256, D] block."""
+    return _encode(cfg, _keys_f32(cfg, g, 1, 256)), _encode(cfg, _values_f32(cfg, g, 1, 256))
+
+
 def batch_chunk(cfg: Config, groups: Sequence[int], chunk: int) -> Tuple[np.ndarray, np.ndarray]:
     """Stacked exact host bytes [len(groups), S, D] for one chunk."""
     ks, vs = zip(*(group_chunk(cfg, g, chunk) for g in groups))
@@ -212,11 +217,11 @@ def custom_keys(shape: Tuple[int, ...], seed: int, dtype: str = "bf16", scale: f
 # Full-size device inputs (torch is only plumbing here)
 # ----------------------------------------------------------------------------
 
-def fill_device(cfg: Config, chunk_rows: int, seed: int, device="cuda", exact_groups: Sequence[int] = (),
-                chunk_index: int = 0, mus=None):
-    """Return device tensors (K, V) of shape [G, chunk_rows, D] following ``cfg``'s
-    recipe with torch's seeded generator; groups listed in ``exact_groups`` carry
-    the exact host bytes of ``group_chunk``/``group_stream`` for ``chunk_index``.
+def fill_device(cfg: Config, rows: int, seed: int, device="cuda", exact=None, mus=None):
+    """Return device tensors (K, V) of shape [G, rows, D] following ``cfg``'s
+    recipe with torch's seeded generator.  ``exact`` maps group -> host (K, V)
+    [rows, D] arrays (from ``group_chunk`` / ``group_stream``) that overwrite
+    those groups, so that they carry the exact bytes the oracle sees.
 
     bf16 tensors are returned as torch.bfloat16, fp32 as torch.float32."""
     import torch
@@ -224,33 +229,35 @@ def fill_device(cfg: Config, chunk_rows: int, seed: int, device="cuda", exact_gr
     gen.manual_seed(seed)
     G = cfg.G
     if cfg.keys == "gauss":
-        k = torch.randn((G, chunk_rows, D), generator=gen, device=device, dtype=torch.float32)
+        k = torch.randn((G, rows, D), generator=gen, device=device, dtype=torch.float32)
     elif cfg.keys == "aniso":
         if mus is None:
-            mus = torch.from_numpy(np.stack([planted_mu(cfg, *cfg.group_lbh(g)[::2])
-                                             for g in range(G)]).astype(np.float32)).to(device)
-        drift = torch.rand((G, chunk_rows, 1), generator=gen, device=device) * 1.5 + 0.5
-        k = torch.randn((G, chunk_rows, D), generator=gen, device=device, dtype=torch.float32)
+            mus = device_mus(cfg, device)
+        drift = torch.rand((G, rows, 1), generator=gen, device=device) * 1.5 + 0.5
+        k = torch.randn((G, rows, D), generator=gen, device=device, dtype=torch.float32)
         k.mul_(0.5).add_(drift * mus[:, None, :])
     elif cfg.keys == "lognorm":
-        k = torch.randn((G, chunk_rows, D), generator=gen, device=device, dtype=torch.float32)
+        k = torch.randn((G, rows, D), generator=gen, device=device, dtype=torch.float32)
         k.div_(k.norm(dim=2, keepdim=True))
-        r = torch.exp(0.5 * torch.randn((G, chunk_rows, 1), generator=gen, device=device))
+        r = torch.exp(0.5 * torch.randn((G, rows, 1), generator=gen, device=device))
         k.mul_(r)
     else:
         raise ValueError(cfg.keys)
-    v = torch.randn((G, chunk_rows, D), generator=gen, device=device, dtype=torch.float32)
+    v = torch.randn((G, rows, D), generator=gen, device=device, dtype=torch.float32)
     if cfg.dtype == "bf16":
         k = k.to(torch.bfloat16)
         v = v.to(torch.bfloat16)
-    for g in exact_groups:
-        if cfg.cid == 3 and chunk_index >= 1:
-            Kh, Vh = group_stream(cfg, g)[chunk_index]
-        else:
-            Kh, Vh = group_chunk(cfg, g, chunk_index)
+    for g, (Kh, Vh) in (exact or {}).items():
         k[g].copy_(host_to_torch(Kh, cfg.dtype))
         v[g].copy_(host_to_torch(Vh, cfg.dtype))
     return k, v
+
+
+def device_mus(cfg: Config, device="cuda"):
+    """[G, D] float32 planted direction of each group (device tensor)."""
+    import torch
+    return torch.from_numpy(np.stack([planted_mu(cfg, *cfg.group_lbh(g)[::2])
+                                      for g in range(cfg.G)]).astype(np.float32)).to(device)
 
 
 def host_to_torch(x: np.ndarray, dtype: str):

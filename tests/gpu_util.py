@@ -1,0 +1,100 @@
+"""Helpers for the GPU parity tests (comparison protocol against the oracle).
+
+Protocol (scores are float32 on both sides, decisions are taken on float32):
+* score check: |s_gpu - s_ref| <= 1e-5 * scale, with scale = the norm (L2) or
+  sum_d |k_d f_d| (projection: the rounding error of a dot product is bounded
+  relative to that sum, not to the result, which may be near zero);
+* lockstep check: the oracle's selection and compaction applied to the GPU's own
+  scores must give the GPU's kept rows, K/V bytes, stored scores and positions
+  bit for bit;
+* independent check: the oracle's own run (its own scores) must keep the same
+  positions, except for swaps between rows whose oracle scores are within the
+  sum of their tolerances (certified near-ties), which are counted.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from kv_cache_token_amd import synth
+
+TOL = 1e-5
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    return (synth.bf16_bits_to_f32(x) if dtype == "bf16" else x).astype(np.float64)
+
+
+def score_scale(K: np.ndarray, dtype: str, mode: str, f=None) -> np.ndarray:
+    """Per-row error scale of K [..., n, D]."""
+    kw = widen(K, dtype)
+    if mode == "l2":
+        return np.sqrt((kw * kw).sum(axis=-1))
+    return np.abs(kw * np.asarray(f, dtype=np.float64)[..., None, :]).sum(axis=-1)
+
+
+def assert_scores_close(s_gpu: np.ndarray, s_ref: np.ndarray, scale: np.ndarray, what: str = "") -> None:
+    err = np.abs(s_gpu.astype(np.float64) - s_ref.astype(np.float64))
+    bound = TOL * scale
+    bad = err > bound
+    assert not bad.any(), "%s: %d scores outside tolerance; worst err %.3g vs bound %.3g" % (
+        what, int(bad.sum()), float(err[bad].max()), float(bound[bad].min()))
+
+
+def certify_near_ties(gpu_pos, ref_pos, s_ref_by_pos: dict, tol_by_pos: dict) -> int:
+    a = sorted(set(gpu_pos) - set(ref_pos))
+    b = sorted(set(ref_pos) - set(gpu_pos))
+    assert len(a) == len(b), "kept sets differ in size"
+    for x in a:
+        for y in b:
+            gap = abs(float(s_ref_by_pos[x]) - float(s_ref_by_pos[y]))
+            assert gap <= tol_by_pos[x] + tol_by_pos[y], \
+                "positions %d/%d differ by %.3g > near-tie bound %.3g" % (x, y, gap, tol_by_pos[x] + tol_by_pos[y])
+    return len(a)
+
+
+def gpu_state(cache, groups):
+    """Host copies of the kept (K, V, s, pos) of the listed groups."""
+    k, v, s, p = cache.kept()
+    out = {}
+    for g in groups:
+        out[g] = (synth.torch_to_host(k[g], "bf16" if cache.shape.dtype == 1 else "f32"),
+                  synth.torch_to_host(v[g], "bf16" if cache.shape.dtype == 1 else "f32"),
+                  s[g].cpu().numpy(), p[g].cpu().numpy())
+    return out
+
+
+def assert_state_equal(gstate: dict, ocache: oracle.OracleCache, idx_of: dict, what: str = "") -> None:
+    for g, (k, v, s, p) in gstate.items():
+        ok, ov, os_, op = ocache.kept(idx_of[g])
+        assert np.array_equal(p, op), "%s: group %d kept positions differ" % (what, g)
+        assert np.array_equal(s, os_), "%s: group %d stored scores differ" % (what, g)
+        assert np.array_equal(k, ok), "%s: group %d K bytes differ" % (what, g)
+        assert np.array_equal(v, ov), "%s: group %d V bytes differ" % (what, g)
+
+
+def assert_state_invariants(cache, tokens: int, recent: int = 0) -> None:
+    """Properties that hold for every group at any size."""
+    import torch
+    k, v, s, p = cache.kept()
+    n = cache.n_kept
+    assert n == min(tokens, cache.budget)
+    if n == 0:
+        return
+    d = p[:, 1:] - p[:, :-1]
+    assert bool((d > 0).all()), "positions must increase strictly"
+    assert int(p.min()) >= 0 and int(p.max()) < tokens
+    ns = min(cache.n_sink, n)
+    if ns:
+        want = torch.arange(ns, device=p.device, dtype=p.dtype)
+        assert bool((p[:, :ns] == want).all()), "sinks must survive"
+    if recent and tokens > cache.budget:
+        want = torch.arange(tokens - recent, tokens, device=p.device, dtype=p.dtype)
+        assert bool((p[:, n - recent:] == want).all()), "the recent window must survive"

@@ -1,0 +1,310 @@
+"""Per-kernel parity of the HIP path against the oracle, through the C ABI.
+
+score: bit-exact on exactly representable inputs, within 1e-5 of the condition
+scale otherwise, and independent of how a block is split.  select: keep_idx
+bit-exact against the oracle's ranking on the same scores, across tile
+boundaries, ties, signed zeros, real infinities and the largest sizes.
+gather / decode: bit-exact against a plain numpy gather / the oracle's rules.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_token_amd import synth
+from tests import refs
+from tests.gpu_util import assert_scores_close, say, score_scale
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_token_amd import _lib
+    _lib.lib()
+
+
+def _t(x, dtype):
+    return synth.host_to_torch(x, dtype).cuda()
+
+
+def _api():
+    from kv_cache_token_amd import api
+    return api
+
+
+def _score_gpu(K, dtype, mode, f_lh, sign, L, B, H):
+    import torch
+    api = _api()
+    G, S = K.shape[0], K.shape[1]
+    out = torch.full((G, S), float("nan"), dtype=torch.float32, device="cuda")
+    fd = None if f_lh is None else torch.from_numpy(np.ascontiguousarray(f_lh, np.float32)).cuda()
+    api.qf_score_keys(_t(K, dtype), api.make_shape(L, B, H, dtype), S, mode, fd, sign, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _group_filters(f_lh, L, B, H):
+    return np.stack([f_lh[g // (B * H), g % H] for g in range(L * B * H)])
+
+
+# --------------------------------------------------------------------------- score
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode,sign", [("l2", 1), ("proj", 1), ("proj", -1)])
+def test_score_bit_exact_on_exact_inputs(dtype, mode, sign):
+    L, B, H, S = 2, 3, 4, 333
+    G = L * B * H
+    say("score exact %s %s %d" % (dtype, mode, sign))
+    K = np.stack([synth.custom_keys((S, D), 300 + g, dtype, kind="int") for g in range(G)])
+    rng = np.random.default_rng(1)
+    f_lh = (rng.integers(-64, 65, size=(L, H, D)) / 64.0).astype(np.float32) if mode == "proj" else None
+    got = _score_gpu(K, dtype, mode, f_lh, sign, L, B, H)
+    fg = _group_filters(f_lh, L, B, H) if mode == "proj" else [None] * G
+    want = np.stack([oracle.score(K[g], mode, fg[g], sign) for g in range(G)])
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode,sign", [("l2", 1), ("proj", 1), ("proj", -1)])
+def test_score_within_tolerance(dtype, mode, sign):
+    L, B, H, S = 3, 2, 8, 1001
+    G = L * B * H
+    say("score tol %s %s %d" % (dtype, mode, sign))
+    K = np.stack([synth.custom_keys((S, D), 400 + g, dtype, scale=10.0 ** (g % 5 - 2)) for g in range(G)])
+    rng = np.random.default_rng(2)
+    f_lh = rng.standard_normal((L, H, D)).astype(np.float32) if mode == "proj" else None
+    if f_lh is not None:
+        f_lh /= np.linalg.norm(f_lh, axis=2, keepdims=True)
+    got = _score_gpu(K, dtype, mode, f_lh, sign, L, B, H)
+    fg = _group_filters(f_lh, L, B, H) if mode == "proj" else [None] * G
+    want = np.stack([oracle.score(K[g], mode, fg[g], sign) for g in range(G)])
+    scale = np.stack([score_scale(K[g], dtype, mode, fg[g]) for g in range(G)])
+    assert_scores_close(got, want, scale, "score")
+    if mode == "proj" and sign == -1:
+        pos = _score_gpu(K, dtype, mode, f_lh, 1, L, B, H)
+        nz = pos != 0
+        assert np.array_equal(got[nz], -pos[nz])          # sign is an exact negation
+
+
+def test_score_independent_of_block_split_and_negative_zero():
+    import torch
+    api = _api()
+    G, S = 7, 515
+    K = np.stack([synth.custom_keys((S, D), 500 + g, "bf16") for g in range(G)])
+    K[:, 3] = 0                                            # zero keys -> +0 scores
+    rng = np.random.default_rng(3)
+    f = rng.standard_normal((1, G, D)).astype(np.float32)
+    whole = _score_gpu(K, "bf16", "proj", f, -1, 1, 1, G)
+    assert np.all(whole[:, 3].view(np.uint32) == 0)
+    for cut in (1, 7, 64, 300):
+        parts = []
+        for a in range(0, S, cut):
+            parts.append(_score_gpu(np.ascontiguousarray(K[:, a:a + cut]), "bf16", "proj", f, -1, 1, 1, G))
+        assert np.array_equal(np.concatenate(parts, axis=1).view(np.uint32), whole.view(np.uint32))
+    # empty blocks launch nothing and succeed
+    out = torch.empty((G, 1), dtype=torch.float32, device="cuda")
+    api.qf_score_keys(_t(K[:, :1], "bf16"), api.make_shape(1, 1, G, "bf16"), 0, "l2", None, 1, out)
+
+
+def test_score_per_group_filters():
+    L, B, H, S = 2, 3, 2, 64
+    G = L * B * H
+    K = np.stack([synth.custom_keys((S, D), 600 + g, "bf16") for g in range(G)])
+    rng = np.random.default_rng(4)
+    fg = rng.standard_normal((G, D)).astype(np.float32)
+    got = _score_gpu(K, "bf16", "proj", fg.reshape(L * B, H, D), 1, L * B, 1, H)
+    want = np.stack([oracle.score(K[g], "proj", fg[g], 1) for g in range(G)])
+    assert_scores_close(got, want, np.stack([score_scale(K[g], "bf16", "proj", fg[g]) for g in range(G)]))
+
+
+# --------------------------------------------------------------------------- select
+
+SELECT_CASES = [
+    # n_kept, S, budget, n_sink, recent, keep
+    (0, 1000, 512, 4, 0, "low"), (0, 1000, 512, 4, 0, "high"),
+    (512, 1, 512, 4, 0, "low"), (512, 512, 512, 4, 0, "high"),
+    (300, 100, 512, 4, 0, "low"),                      # under budget: identity
+    (0, 1024, 1023, 0, 0, "high"), (1, 1024, 1024, 0, 1, "low"),   # tile edges 1024/1025
+    (1024, 1024, 1024, 3, 7, "low"), (1024, 1025, 1024, 3, 7, "high"),
+    (2048, 1, 2048, 4, 512, "low"), (2048, 2049, 2048, 4, 512, "low"),
+    (4096, 4096, 4096, 4, 0, "low"), (4096, 4096, 4096, 4, 0, "high"),
+    (0, 8193, 8192, 4, 0, "high"), (8192, 8192, 8192, 4, 0, "high"), (8192, 8192, 8192, 4, 100, "low"),
+    (0, 16384, 8192, 0, 0, "low"), (3, 5, 4, 1, 2, "high"), (0, 4097, 1, 0, 0, "low"),
+    (100, 1949, 2000, 10, 30, "high"), (7, 77, 50, 49, 0, "low"),
+]
+
+
+def _select_gpu(sk, sn, n_kept, S, budget, n_sink, recent, keep):
+    import torch
+    api = _api()
+    G = sn.shape[0]
+    s_kept = torch.zeros((G, budget), dtype=torch.float32, device="cuda")
+    if n_kept:
+        s_kept[:, :n_kept] = torch.from_numpy(sk).cuda()
+    s_new = torch.from_numpy(np.ascontiguousarray(sn)).cuda() if S else torch.zeros((G, 1), device="cuda")
+    idx = torch.full((G, budget), -7, dtype=torch.int32, device="cuda")
+    api.kv_evict_topk(s_kept, s_new, api.make_shape(1, 1, G, "bf16"), n_kept, S,
+                      api.make_params(budget, n_sink, recent, keep), idx)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=[str(c) for c in SELECT_CASES])
+@pytest.mark.parametrize("dist", ["gauss", "ties"])
+def test_select_matches_oracle(case, dist):
+    n_kept, S, budget, n_sink, recent, keep = case
+    say("select %s %s" % (case, dist))
+    G = 3
+    rng = np.random.default_rng(zlib.crc32((str(case) + dist).encode()))
+    n_total = n_kept + S
+    if dist == "gauss":
+        s = rng.standard_normal((G, n_total)).astype(np.float32)
+    else:
+        s = rng.integers(-3, 4, size=(G, n_total)).astype(np.float32)
+        s[s == 0] = np.where(rng.random((s == 0).sum()) < 0.5, -0.0, 0.0)
+    idx = _select_gpu(s[:, :n_kept], s[:, n_kept:], n_kept, S, budget, n_sink, recent, keep)
+    n_out = min(n_total, budget)
+    for g in range(G):
+        want = oracle.select(s[g], budget, n_sink, recent, keep)
+        assert np.array_equal(idx[g, :n_out], want), "group %d" % g
+        assert np.all(idx[g, n_out:] == -7)                  # nothing written past n_out
+
+
+def test_select_real_infinities_rank_below_protected_rows():
+    S, budget = 40, 10
+    s = np.zeros((2, S), dtype=np.float32)
+    s[0, 5:20] = np.inf
+    s[1, :] = -np.inf
+    s[1, 30] = 1.0
+    for keep in ("high", "low"):
+        idx = _select_gpu(s[:, :0], s, 0, S, budget, 2, 3, keep)
+        for g in range(2):
+            want = refs.lexsort_select(s[g], budget, 2, 3, keep)
+            assert np.array_equal(idx[g], want)
+
+
+# --------------------------------------------------------------------------- gather
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_kept,S,budget", [(0, 300, 128), (128, 200, 128), (100, 28, 128), (128, 1, 128),
+                                             (4096, 4096, 4096), (37, 91, 64)])
+def test_gather_bit_exact(dtype, n_kept, S, budget):
+    import torch
+    api = _api()
+    say("gather %s %d %d %d" % (dtype, n_kept, S, budget))
+    G, n_sink, recent = 5, 2, 3
+    shape, params = api.make_shape(1, 1, G, dtype), api.make_params(budget, n_sink, recent, "low")
+    rng = np.random.default_rng(n_kept + S)
+    Kc = synth.custom_keys((G, budget, D), 700, dtype)
+    Vc = synth.custom_keys((G, budget, D), 701, dtype)
+    Kn = synth.custom_keys((G, S, D), 702, dtype)
+    Vn = synth.custom_keys((G, S, D), 703, dtype)
+    sc = rng.standard_normal((G, budget)).astype(np.float32)
+    pc = np.sort(rng.choice(10 ** 6, size=(G, budget), replace=False), axis=1).astype(np.int32)
+    sn = rng.standard_normal((G, S)).astype(np.float32)
+    base = 10 ** 6 + 17
+    dK, dV, dS, dP = _t(Kc, dtype), _t(Vc, dtype), torch.from_numpy(sc).cuda(), torch.from_numpy(pc).cuda()
+    dKn, dVn, dSn = _t(Kn, dtype), _t(Vn, dtype), torch.from_numpy(sn).cuda()
+    idx = torch.zeros((G, budget), dtype=torch.int32, device="cuda")
+    api.kv_evict_topk(dS, dSn, shape, n_kept, S, params, idx)
+    outs = [torch.zeros_like(dK), torch.zeros_like(dV), torch.zeros_like(dS), torch.zeros_like(dP)]
+    api.kv_compact_gather(dK, dV, dS, dP, dKn, dVn, dSn, base, idx, shape, n_kept, S, params, *outs)
+    torch.cuda.synchronize()
+    n_out = min(n_kept + S, budget)
+    I = idx.cpu().numpy()
+    catK = np.concatenate([Kc[:, :n_kept], Kn], axis=1)
+    catV = np.concatenate([Vc[:, :n_kept], Vn], axis=1)
+    catS = np.concatenate([sc[:, :n_kept], sn], axis=1)
+    catP = np.concatenate([pc[:, :n_kept], np.broadcast_to(base + np.arange(S, dtype=np.int32), (G, S))], axis=1)
+    for g in range(G):
+        want = oracle.select(catS[g], budget, n_sink, recent, "low")
+        assert np.array_equal(I[g, :n_out], want)
+        assert np.array_equal(synth.torch_to_host(outs[0][g, :n_out], dtype), catK[g, want])
+        assert np.array_equal(synth.torch_to_host(outs[1][g, :n_out], dtype), catV[g, want])
+        assert np.array_equal(outs[2][g, :n_out].cpu().numpy(), catS[g, want])
+        assert np.array_equal(outs[3][g, :n_out].cpu().numpy(), catP[g, want])
+    if n_kept + S <= budget:            # in-place append: only the incoming rows move
+        api.kv_compact_gather(dK, dV, dS, dP, dKn, dVn, dSn, base, None, shape, n_kept, S, params,
+                              dK, dV, dS, dP)
+        torch.cuda.synchronize()
+        for g in range(G):
+            assert np.array_equal(synth.torch_to_host(dK[g, :n_out], dtype), catK[g])
+            assert np.array_equal(synth.torch_to_host(dV[g, :n_out], dtype), catV[g])
+            assert np.array_equal(dP[g, :n_out].cpu().numpy(), catP[g])
+            assert np.array_equal(synth.torch_to_host(dK[g, n_out:], dtype), Kc[g, n_out:])  # untouched
+
+
+# --------------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("recent,keep", [(0, "low"), (1, "high"), (8, "low"), (8, "high")])
+def test_decode_inplace_lockstep_with_oracle(dtype, recent, keep):
+    import torch
+    from kv_cache_token_amd.cache import EvictingCache
+    say("decode %s %d %s" % (dtype, recent, keep))
+    G, T, budget, n_sink = 4, 300, 64, 2
+    K = np.stack([synth.custom_keys((T, D), 800 + g, dtype, kind="dup") for g in range(G)])
+    V = np.stack([synth.custom_keys((T, D), 900 + g, dtype) for g in range(G)])
+    dK, dV = _t(K, dtype), _t(V, dtype)
+    c = EvictingCache(1, 1, G, budget, n_sink, recent, keep, "l2", dtype=dtype)
+    o = oracle.OracleCache(G, D, dtype, budget, n_sink, recent, keep)
+    for t in range(T):
+        c.update(dK[:, t:t + 1].contiguous(), dV[:, t:t + 1].contiguous())
+        s_gpu = c.last_scores().cpu().numpy()
+        o.update(K[:, t:t + 1], V[:, t:t + 1], scores_in=s_gpu)
+        if t % 37 == 0 or t == T - 1:
+            k, v, s, p = c.kept()
+            for g in range(G):
+                ok, ov, os_, op = o.kept(g)
+                assert np.array_equal(p[g].cpu().numpy(), op), (t, g)
+                assert np.array_equal(s[g].cpu().numpy(), os_), (t, g)
+                assert np.array_equal(synth.torch_to_host(k[g], dtype), ok), (t, g)
+                assert np.array_equal(synth.torch_to_host(v[g], dtype), ov), (t, g)
+    torch.cuda.synchronize()
+
+
+def test_decode_and_block_paths_agree_on_gpu():
+    """With scores fixed at insertion the kept set is a closed form of the whole
+    stream, so single-token decode and block updates must agree bit for bit."""
+    from kv_cache_token_amd.cache import EvictingCache
+    G, T, budget, n_sink, recent = 6, 700, 97, 3, 11
+    K = np.stack([synth.custom_keys((T, D), 1000 + g, "bf16") for g in range(G)])
+    dK = _t(K, "bf16")
+    states = []
+    for chunk in (T, 128, 1):
+        c = EvictingCache(1, 1, G, budget, n_sink, recent, "low", "l2")
+        for a in range(0, T, chunk):
+            c.update(dK[:, a:a + chunk].contiguous(), dK[:, a:a + chunk].contiguous())
+        states.append([x.cpu() for x in c.kept()])
+    for st in states[1:]:
+        for x, y in zip(states[0], st):
+            assert _bits_equal(x, y)
+
+
+def _bits_equal(x, y) -> bool:
+    import torch
+    if x.dtype in (torch.bfloat16, torch.float32):
+        x, y = x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32), \
+            y.view(torch.int16 if y.dtype == torch.bfloat16 else torch.int32)
+    return x.shape == y.shape and bool((x == y).all())
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    import torch
+    api = _api()
+    from kv_cache_token_amd._lib import KvxError
+    s = torch.zeros((2, 8), device="cuda")
+    idx = torch.zeros((2, 8), dtype=torch.int32, device="cuda")
+    sh = api.make_shape(1, 1, 2, "bf16")
+    with pytest.raises(KvxError):
+        api.kv_evict_topk(s, s, sh, 0, 8, api.make_params(8, 4, 4, "low"), idx)     # sinks + recent >= budget
+    with pytest.raises(KvxError):
+        api.kv_evict_topk(s, s, sh, 9, 8, api.make_params(8, 1, 0, "low"), idx)     # n_kept > budget
+    with pytest.raises(KvxError):
+        api.qf_score_keys(torch.zeros((2, 8, D), dtype=torch.bfloat16, device="cuda"), sh, 8, "proj", None, 1, s)
