@@ -125,8 +125,8 @@ class EvictingCache:
     def update(self, k_new, v_new) -> None:
         """Absorb one block: k_new, v_new [G, S, D] (or [L, B, H, S, D]) contiguous."""
         S = k_new.shape[-2]
-        k_new = k_new.reshape(self.G, S, D)
-        v_new = v_new.reshape(self.G, S, D)
+        k_new = k_new.contiguous().reshape(self.G, S, D)
+        v_new = v_new.contiguous().reshape(self.G, S, D)
         if S == 0:
             return
         if self.mode == "proj" and self.filters is None:

@@ -306,5 +306,8 @@ def test_invalid_arguments_are_rejected_before_launch():
         api.kv_evict_topk(s, s, sh, 0, 8, api.make_params(8, 4, 4, "low"), idx)     # sinks + recent >= budget
     with pytest.raises(KvxError):
         api.kv_evict_topk(s, s, sh, 9, 8, api.make_params(8, 1, 0, "low"), idx)     # n_kept > budget
-    with pytest.raises(KvxError):
+    with pytest.raises(ValueError):       # the binding refuses before the library is called
         api.qf_score_keys(torch.zeros((2, 8, D), dtype=torch.bfloat16, device="cuda"), sh, 8, "proj", None, 1, s)
+    with pytest.raises(KvxError):         # and the library itself refuses a bad sign
+        api.qf_score_keys(torch.zeros((2, 8, D), dtype=torch.bfloat16, device="cuda"), sh, 8, "proj",
+                          torch.zeros((1, 2, D), device="cuda"), 3, s)
