@@ -81,17 +81,35 @@ def _G(shape: KvxShape) -> int:
     return shape.L * shape.B * shape.H
 
 
+def _dispatch(fn: str, args, prepare: bool):
+    """Call the library now, or (prepare=True) return (function, args) so that a
+    validated call can be replayed later without re-marshalling."""
+    if prepare:
+        return getattr(_lib.lib(), fn), tuple(args)
+    call(fn, *args)
+    return None
+
+
+def run_prepared(calls) -> None:
+    """Replay prepared calls in order (each was validated when prepared)."""
+    for f, args in calls:
+        rc = f(*args)
+        if rc != 0:
+            _lib.check(f.__name__, rc)
+
+
 # --------------------------------------------------------------------------- device
 
 
-def qf_score_keys(k_new, shape: KvxShape, S: int, mode, filters, sign: int, s_new, stream=None) -> None:
+def qf_score_keys(k_new, shape: KvxShape, S: int, mode, filters, sign: int, s_new, stream=None,
+                  prepare: bool = False):
     """Score G*S incoming rows into s_new [G, S] (float32)."""
     torch = _torch()
     G, m = _G(shape), mode_code(mode)
     kp = _dev(k_new, "k_new", torch_dtype(shape.dtype), G * S * D)
     fp = _dev(filters, "filters", torch.float32, shape.L * shape.H * D, allow_none=(m == KVX_SCORE_L2))
     sp = _dev(s_new, "s_new", torch.float32, G * S)
-    call("qf_score_keys", kp, shape, S, m, fp, sign, sp, _stream(stream))
+    return _dispatch("qf_score_keys", (kp, shape, S, m, fp, sign, sp, _stream(stream)), prepare)
 
 
 def kv_evict_workspace_size(shape: KvxShape, n_kept: int, S: int, params: KvxParams) -> int:
@@ -101,20 +119,20 @@ def kv_evict_workspace_size(shape: KvxShape, n_kept: int, S: int, params: KvxPar
 
 
 def kv_evict_topk(s_kept, s_new, shape: KvxShape, n_kept: int, S: int, params: KvxParams, keep_idx,
-                  ws=None, stream=None) -> None:
+                  ws=None, stream=None, prepare: bool = False):
     torch = _torch()
     G = _G(shape)
     kp = _dev(s_kept, "s_kept", torch.float32, G * params.budget, allow_none=(n_kept == 0))
     np_ = _dev(s_new, "s_new", torch.float32, G * S, allow_none=(S == 0))
     ip = _dev(keep_idx, "keep_idx", torch.int32, G * params.budget)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    call("kv_evict_topk", kp, np_, shape, n_kept, S, params, ip, None if ws is None else ws.data_ptr(), wsb,
-         _stream(stream))
+    return _dispatch("kv_evict_topk", (kp, np_, shape, n_kept, S, params, ip,
+                                       None if ws is None else ws.data_ptr(), wsb, _stream(stream)), prepare)
 
 
 def kv_compact_gather(k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, pos_base: int, keep_idx,
                       shape: KvxShape, n_kept: int, S: int, params: KvxParams, k_out, v_out, s_out, pos_out,
-                      stream=None) -> None:
+                      stream=None, prepare: bool = False):
     torch = _torch()
     G, td, cap = _G(shape), torch_dtype(shape.dtype), params.budget
     evict = n_kept + S > cap
@@ -135,18 +153,18 @@ def kv_compact_gather(k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, pos
         _dev(pos_out, "pos_out", torch.int32, G * cap),
         _stream(stream),
     ]
-    call("kv_compact_gather", *args)
+    return _dispatch("kv_compact_gather", args, prepare)
 
 
 def kv_evict_one_inplace(k_cache, v_cache, s_cache, pos_cache, k_new, v_new, s_new, pos_base: int,
-                         shape: KvxShape, n_kept: int, params: KvxParams, stream=None) -> None:
+                         shape: KvxShape, n_kept: int, params: KvxParams, stream=None, prepare: bool = False):
     torch = _torch()
     G, td, cap = _G(shape), torch_dtype(shape.dtype), params.budget
-    call("kv_evict_one_inplace",
-         _dev(k_cache, "k_cache", td, G * cap * D), _dev(v_cache, "v_cache", td, G * cap * D),
-         _dev(s_cache, "s_cache", torch.float32, G * cap), _dev(pos_cache, "pos_cache", torch.int32, G * cap),
-         _dev(k_new, "k_new", td, G * D), _dev(v_new, "v_new", td, G * D),
-         _dev(s_new, "s_new", torch.float32, G), pos_base, shape, n_kept, params, _stream(stream))
+    args = (_dev(k_cache, "k_cache", td, G * cap * D), _dev(v_cache, "v_cache", td, G * cap * D),
+            _dev(s_cache, "s_cache", torch.float32, G * cap), _dev(pos_cache, "pos_cache", torch.int32, G * cap),
+            _dev(k_new, "k_new", td, G * D), _dev(v_new, "v_new", td, G * D),
+            _dev(s_new, "s_new", torch.float32, G), pos_base, shape, n_kept, params, _stream(stream))
+    return _dispatch("kv_evict_one_inplace", args, prepare)
 
 
 # --------------------------------------------------------------------------- host

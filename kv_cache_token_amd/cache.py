@@ -123,29 +123,81 @@ class EvictingCache:
         return self._s_new
 
     def update(self, k_new, v_new) -> None:
-        """Absorb one block: k_new, v_new [G, S, D] (or [L, B, H, S, D]) contiguous."""
+        """Absorb one block: k_new, v_new [G, S, D] (or [L, B, H, S, D])."""
+        self._step(k_new, v_new, prepare=False)
+
+    def _step(self, k_new, v_new, prepare: bool):
         S = k_new.shape[-2]
         k_new = k_new.contiguous().reshape(self.G, S, D)
         v_new = v_new.contiguous().reshape(self.G, S, D)
+        calls = []
         if S == 0:
-            return
+            return calls, (k_new, v_new)
         if self.mode == "proj" and self.filters is None:
+            if prepare:
+                raise RuntimeError("freeze the fallback filters (one update) before planning")
             self._freeze_fallback(k_new)
         s_new = self._scores(S)
-        api.qf_score_keys(k_new, self.score_shape, S, self.mode, self.filters, self.sign, s_new, self.stream)
+        calls.append(api.qf_score_keys(k_new, self.score_shape, S, self.mode, self.filters, self.sign, s_new,
+                                       self.stream, prepare=prepare))
         k, v, s, p = self._bufs[self._cur]
         nk, pos_base = self.n_kept, self.tokens_seen
         if S == 1:
-            api.kv_evict_one_inplace(k, v, s, p, k_new, v_new, s_new, pos_base, self.shape, nk, self.params,
-                                     self.stream)
+            calls.append(api.kv_evict_one_inplace(k, v, s, p, k_new, v_new, s_new, pos_base, self.shape, nk,
+                                                  self.params, self.stream, prepare=prepare))
         elif nk + S <= self.budget:
-            api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, None, self.shape, nk, S,
-                                  self.params, k, v, s, p, self.stream)
+            calls.append(api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, None, self.shape, nk, S,
+                                               self.params, k, v, s, p, self.stream, prepare=prepare))
         else:
-            api.kv_evict_topk(s, s_new, self.shape, nk, S, self.params, self.keep_idx, None, self.stream)
+            calls.append(api.kv_evict_topk(s, s_new, self.shape, nk, S, self.params, self.keep_idx, None,
+                                           self.stream, prepare=prepare))
             ko, vo, so, po = self._bufs[1 - self._cur]
-            api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, self.keep_idx, self.shape, nk, S,
-                                  self.params, ko, vo, so, po, self.stream)
+            calls.append(api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, self.keep_idx,
+                                               self.shape, nk, S, self.params, ko, vo, so, po, self.stream,
+                                               prepare=prepare))
             self._cur = 1 - self._cur
         self.n_kept = min(nk + S, self.budget)
         self.tokens_seen += S
+        return calls, (k_new, v_new, s_new)
+
+    def plan(self, blocks) -> "StreamPlan":
+        """Validate and record, once, the library calls that absorb `blocks`
+        (a list of (K, V) device tensors) into an empty cache.  The plan replays
+        them with no per-call marshalling (or inside a captured HIP graph); it
+        keeps the tensors it points at alive.  The cache is left empty."""
+        self.n_kept, self.tokens_seen, self._cur = 0, 0, 0
+        calls, keep = [], []
+        for k, v in blocks:
+            c, refs = self._step(k, v, prepare=True)
+            calls += c
+            keep.append(refs)
+        final = (self.n_kept, self.tokens_seen, self._cur)
+        self.n_kept, self.tokens_seen, self._cur = 0, 0, 0
+        return StreamPlan(self, calls, final, keep)
+
+
+class StreamPlan:
+    """Prepared library calls of a whole block stream (see EvictingCache.plan)."""
+
+    def __init__(self, cache: EvictingCache, calls, final, keepalive):
+        self.cache, self.calls, self.final, self._keep = cache, calls, final, keepalive
+
+    @property
+    def names(self):
+        return [f.__name__ for f, _ in self.calls]
+
+    def run(self, hook=None) -> None:
+        """Enqueue every call, starting from an empty cache; hook(i, name, when)
+        with when in ("before", "after") is called around each call."""
+        c = self.cache
+        c.n_kept, c.tokens_seen, c._cur = 0, 0, 0
+        for i, (f, args) in enumerate(self.calls):
+            if hook:
+                hook(i, f.__name__, "before")
+            rc = f(*args)
+            if rc != 0:
+                from . import _lib
+                _lib.check(f.__name__, rc)
+            if hook:
+                hook(i, f.__name__, "after")
+        c.n_kept, c.tokens_seen, c._cur = self.final
