@@ -30,6 +30,12 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 D = 128
+KERNEL_SRC = os.path.join(ROOT, "kv_cache_token_amd", "csrc", "kvx_device.hip")
+# HBM bytes per evicting compaction launch, from the two rocprofv3 counter runs
+# (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, factors from a 1 GiB device copy) in
+# profiles/c4_chunked_prefill_32k_hbm_counters.md, valid only for the kernel
+# source they were taken on.
+MEASURED_TRAFFIC = {"kernel_src_sha256_16": "fcba0c27a0cb1391", "bytes_per_launch": 977377568}
 
 
 def log(*a):
@@ -228,8 +234,11 @@ def main():
         mean_ms = sum(evict_ms) / len(evict_ms)
         bytes_per_launch = sum(gather_bytes) / len(gather_bytes)
         achieved = bytes_per_launch / (mean_ms * 1e-3) / 1e9
+        import hashlib
+        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+        traffic = MEASURED_TRAFFIC["bytes_per_launch"] if sha == MEASURED_TRAFFIC["kernel_src_sha256_16"] else None
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic, "traffic_unit": "bytes/launch",
                 "kernel": "kv_compact_gather (evicting calls)", "launches": len(evict_ms),
                 "mean_launch_us": round(mean_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(bytes_per_launch)}
     tokens_per_step = len(cfg.scorers) * cfg.tokens

@@ -18,27 +18,30 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-I", INCLUDE, "-I", CSRC]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
+def build(verbose: bool = False, defines=(), out: str = LIB, objdir: str = CSRC) -> str:
+    """Compile every source and link the shared library; returns its path.
+    `defines` are extra -D flags (the kernels' compile-time tuning knobs)."""
     objs = []
+    dflags = ["-D" + d for d in defines]
+    os.makedirs(objdir, exist_ok=True)
     for src in SOURCES:
         path = os.path.join(CSRC, src)
-        obj = os.path.join(CSRC, src + ".o")
+        obj = os.path.join(objdir, src + ".o")
         if src.endswith(".hip"):
-            cmd = [HIPCC, *DEVICE_FLAGS, *COMMON, "-c", path, "-o", obj]
+            cmd = [HIPCC, *DEVICE_FLAGS, *COMMON, *dflags, "-c", path, "-o", obj]
         else:
             cmd = ["g++", *COMMON, "-Wall", "-Wextra", "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
         subprocess.check_call(cmd)
         objs.append(obj)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *DEVICE_FLAGS, "-shared", "-fPIC", *objs, "-o", tmp, "-lpthread"]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

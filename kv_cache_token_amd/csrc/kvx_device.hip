@@ -27,8 +27,59 @@ struct Row {
     static constexpr int kElemsPerLane = 16 / kElemBytes;
 };
 
-__device__ __forceinline__ uint4 ld16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
-__device__ __forceinline__ void st16(char *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+// Tuning knobs (compile-time): rows in flight per lane and cache hints.
+#ifndef KVX_SCORE_U
+#define KVX_SCORE_U 4
+#endif
+#ifndef KVX_SCORE_BLOCKS_PER_CU
+#define KVX_SCORE_BLOCKS_PER_CU 0  // 0: one block per row tile, no grid-stride cap
+#endif
+#ifndef KVX_GATHER_U
+#define KVX_GATHER_U 1
+#endif
+#ifndef KVX_GATHER_BLOCK
+#define KVX_GATHER_BLOCK 256
+#endif
+#ifndef KVX_SCORE_BLOCK
+#define KVX_SCORE_BLOCK 256
+#endif
+// Streaming (non-temporal) hints per kernel: K/V rows are touched once per
+// call, so they need not displace other data in the caches.
+#ifndef KVX_SCORE_NT_LOAD
+#define KVX_SCORE_NT_LOAD 1
+#endif
+#ifndef KVX_GATHER_NT_LOAD
+#define KVX_GATHER_NT_LOAD 1
+#endif
+#ifndef KVX_GATHER_NT_STORE
+#define KVX_GATHER_NT_STORE 1
+#endif
+#ifndef KVX_DECODE_NT
+#define KVX_DECODE_NT 0
+#endif
+#ifndef KVX_SELECT_NT
+#define KVX_SELECT_NT 1024
+#endif
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+template <bool NT = false>
+__device__ __forceinline__ uint4 ld16(const char *p) {
+    if constexpr (NT)
+        return to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
+    else
+        return to_uint4(*reinterpret_cast<const u32x4 *>(p));
+}
+template <bool NT = false>
+__device__ __forceinline__ void st16(char *p, uint4 v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    if constexpr (NT)
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+    else
+        *reinterpret_cast<u32x4 *>(p) = w;
+}
 
 // Widen the 16 bytes a lane holds to float32 (exact for both element types).
 template <int DT>
@@ -66,7 +117,7 @@ __device__ __forceinline__ uint32_t select_key(float s, int keep_low) {
 // tile it falls in or on the grid.
 // ---------------------------------------------------------------------------
 template <int DT, int MODE, int U>
-__global__ __launch_bounds__(256) void score_kernel(const char *__restrict__ k, uint32_t n_rows,
+__global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_kernel(const char *__restrict__ k, uint32_t n_rows,
                                                     uint32_t S, uint32_t BH, uint32_t H,
                                                     const float *__restrict__ filt, float sign,
                                                     float *__restrict__ out) {
@@ -76,13 +127,14 @@ __global__ __launch_bounds__(256) void score_kernel(const char *__restrict__ k, 
     const uint32_t sub = lane / R::kLanes;
     const uint32_t part = lane % R::kLanes;
     const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const uint32_t row0 = wave * (kRowsPerLoad * U);
-
+    const uint32_t wave_stride = gridDim.x * (blockDim.x >> 6) * (kRowsPerLoad * U);
+    for (uint32_t row0 = wave * (kRowsPerLoad * U); row0 < n_rows; row0 += wave_stride) {
     uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t r = row0 + u * kRowsPerLoad + sub;
-        raw[u] = r < n_rows ? ld16(k + (size_t)r * R::kBytes + part * 16) : make_uint4(0, 0, 0, 0);
+        raw[u] = r < n_rows ? ld16<KVX_SCORE_NT_LOAD>(k + (size_t)r * R::kBytes + part * 16)
+                            : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -117,19 +169,20 @@ __global__ __launch_bounds__(256) void score_kernel(const char *__restrict__ k, 
             out[r] = s + 0.0f;  // -0 -> +0
         }
     }
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Steps 2-3: selection.  One 1024-thread workgroup per group.  Thread t holds
-// the keys of rows t, t + 1024, ... (M of them) in registers, so every load is
+// Steps 2-3: selection.  One workgroup of NT threads per group.  Thread t holds
+// the keys of rows t, t + NT, ... (M of them) in registers, so every load is
 // coalesced.  The budget-th largest key tau is found with four 8-bit radix
 // passes over an LDS histogram; then the kept rows are those with key > tau
 // plus the first `quota` rows (in row order) with key == tau, and their
 // indices are written in row order using per-64-row chunk counts.
 // Protected rows get key 0xFFFFFFFF, above every real score's key.
 // ---------------------------------------------------------------------------
-template <int M>
-__global__ __launch_bounds__(1024) void select_kernel(const float *__restrict__ s_kept,
+template <int M, int NT>
+__global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_kept,
                                                       const float *__restrict__ s_new, int n_kept,
                                                       int S, int budget, int n_sink, int recent,
                                                       int keep_low, int32_t *__restrict__ keep_idx) {
@@ -138,7 +191,7 @@ __global__ __launch_bounds__(1024) void select_kernel(const float *__restrict__ 
     const int n_total = n_kept + S;
     int32_t *out = keep_idx + (size_t)g * budget;
     if (n_total <= budget) {
-        for (int r = t; r < n_total; r += 1024) out[r] = r;
+        for (int r = t; r < n_total; r += NT) out[r] = r;
         return;
     }
     const float *sk = s_kept + (size_t)g * budget;
@@ -147,7 +200,7 @@ __global__ __launch_bounds__(1024) void select_kernel(const float *__restrict__ 
     uint32_t key[M];
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-        const int r = i * 1024 + t;
+        const int r = i * NT + t;
         uint32_t kk = 0;
         if (r < n_total) {
             const float s = r < n_kept ? sk[r] : sn[r - n_kept];
@@ -168,20 +221,23 @@ __global__ __launch_bounds__(1024) void select_kernel(const float *__restrict__ 
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < M; ++i) {
-            const int r = i * 1024 + t;
+            const int r = i * NT + t;
             bool act = r < n_total && (key[i] & pmask) == prefix;
             const uint32_t d = (key[i] >> shift) & 0xFFu;
-            // A few rounds of wave-aggregated increments take the common digits
-            // (scores cluster, so one digit often covers most of a wave).
+            // Wave-aggregated increments while the leading digit covers many
+            // lanes (scores cluster, so one digit often covers most of a wave);
+            // once the digits spread, one atomic per lane.
             for (int it = 0; it < 4; ++it) {
                 const uint64_t am = __ballot(act);
                 if (am == 0) break;
                 const int leader = __ffsll((unsigned long long)am) - 1;
-                const uint32_t ld = __shfl(d, leader);
+                const uint32_t ld = __builtin_amdgcn_readlane(d, leader);
                 const bool mine = act && d == ld;
                 const uint64_t m = __ballot(mine);
-                if (lane == leader) atomicAdd(&hist[ld], (uint32_t)__popcll(m));
+                const uint32_t cnt = (uint32_t)__popcll(m);
+                if (lane == leader) atomicAdd(&hist[ld], cnt);
                 if (mine) act = false;
+                if (cnt < 8) break;
             }
             if (act) atomicAdd(&hist[d], 1u);
         }
@@ -229,7 +285,7 @@ __global__ __launch_bounds__(1024) void select_kernel(const float *__restrict__ 
     const int nchunks = (n_total + 63) >> 6;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-        const int c = i * 16 + w;
+        const int c = i * (NT / 64) + w;
         const int r = c * 64 + lane;
         const bool valid = r < n_total;
         const uint64_t gm = __ballot(valid && key[i] > tau);
@@ -264,7 +320,7 @@ __global__ __launch_bounds__(1024) void select_kernel(const float *__restrict__ 
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-        const int c = i * 16 + w;
+        const int c = i * (NT / 64) + w;
         const int r = c * 64 + lane;
         const bool valid = r < n_total;
         const uint64_t gm = __ballot(valid && key[i] > tau);
@@ -292,7 +348,7 @@ __global__ __launch_bounds__(1024) void select_kernel(const float *__restrict__ 
 // keep_idx == nullptr means the identity (nothing evicted).
 // ---------------------------------------------------------------------------
 template <int DT, int U>
-__global__ __launch_bounds__(256) void gather_kernel(
+__global__ __launch_bounds__(KVX_GATHER_BLOCK) void gather_kernel(
     const char *__restrict__ k_kept, const char *__restrict__ v_kept,
     const float *__restrict__ s_kept, const int32_t *__restrict__ pos_kept,
     const char *__restrict__ k_new, const char *__restrict__ v_new,
@@ -300,7 +356,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
     int n_kept, int S, int budget, int j0, int n_out, int blocks_per_group, char *__restrict__ k_out,
     char *__restrict__ v_out, float *__restrict__ s_out, int32_t *__restrict__ pos_out) {
     using R = Row<DT>;
-    constexpr int kRowsPerPass = 256 / R::kLanes;
+    constexpr int kRowsPerPass = KVX_GATHER_BLOCK / R::kLanes;
     const int g = blockIdx.x / blocks_per_group;
     const int b = blockIdx.x - g * blocks_per_group;
     const int part = threadIdx.x % R::kLanes;
@@ -323,8 +379,8 @@ __global__ __launch_bounds__(256) void gather_kernel(
                                           : (new_row0 + (r - n_kept)) * R::kBytes;
             const char *kb = r < n_kept ? k_kept : k_new;
             const char *vb = r < n_kept ? v_kept : v_new;
-            kr[u] = ld16(kb + off + part * 16);
-            vr[u] = ld16(vb + off + part * 16);
+            kr[u] = ld16<KVX_GATHER_NT_LOAD>(kb + off + part * 16);
+            vr[u] = ld16<KVX_GATHER_NT_LOAD>(vb + off + part * 16);
         }
     }
 #pragma unroll
@@ -332,8 +388,8 @@ __global__ __launch_bounds__(256) void gather_kernel(
         const int j = jb + u * kRowsPerPass + sub;
         if (j < n_out) {
             const size_t off = (cache_row0 + j) * R::kBytes + part * 16;
-            st16(k_out + off, kr[u]);
-            st16(v_out + off, vr[u]);
+            st16<KVX_GATHER_NT_STORE>(k_out + off, kr[u]);
+            st16<KVX_GATHER_NT_STORE>(v_out + off, vr[u]);
             if (part == 0) {
                 const int r = src[u];
                 s_out[cache_row0 + j] = r < n_kept ? s_kept[cache_row0 + r] : s_new[new_row0 + (r - n_kept)];
@@ -408,7 +464,7 @@ __global__ __launch_bounds__(256) void evict_one_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int src = c0 + u * kRowsPerPass + sub;
-                if (src < budget) d[u] = ld16(base + (size_t)src * R::kBytes + part * 16);
+                if (src < budget) d[u] = ld16<KVX_DECODE_NT>(base + (size_t)src * R::kBytes + part * 16);
             }
             if (t < C && c0 + t < budget) {
                 sv = sc[c0 + t];
@@ -419,7 +475,7 @@ __global__ __launch_bounds__(256) void evict_one_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int src = c0 + u * kRowsPerPass + sub;
-                if (src < budget) st16(base + (size_t)(src - 1) * R::kBytes + part * 16, d[u]);
+                if (src < budget) st16<KVX_DECODE_NT>(base + (size_t)(src - 1) * R::kBytes + part * 16, d[u]);
             }
             if (t < C && c0 + t < budget) {
                 sc[c0 + t - 1] = sv;
@@ -496,16 +552,17 @@ int validate_select_sizes(const kvx_shape &shape, int64_t n_kept, int64_t S, con
 template <int DT>
 int launch_score(const void *k_new, int64_t G, const kvx_shape &sh, int64_t S, int32_t mode,
                  const float *filters, int32_t sign, float *s_new, hipStream_t st) {
-    constexpr int U = 4;
-    constexpr int kRowsPerBlock = 4 * (64 / Row<DT>::kLanes) * U;
+    constexpr int U = KVX_SCORE_U;
+    constexpr int kRowsPerBlock = (KVX_SCORE_BLOCK / 64) * (64 / Row<DT>::kLanes) * U;
     const uint32_t n_rows = (uint32_t)(G * S);
-    const uint32_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    uint32_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    if (KVX_SCORE_BLOCKS_PER_CU > 0 && blocks > 256u * KVX_SCORE_BLOCKS_PER_CU) blocks = 256u * KVX_SCORE_BLOCKS_PER_CU;
     const uint32_t BH = (uint32_t)(sh.B * sh.H), H = (uint32_t)sh.H;
     if (mode == KVX_SCORE_L2)
-        score_kernel<DT, KVX_SCORE_L2, U><<<blocks, 256, 0, st>>>(
+        score_kernel<DT, KVX_SCORE_L2, U><<<blocks, KVX_SCORE_BLOCK, 0, st>>>(
             (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, 1.0f, s_new);
     else
-        score_kernel<DT, KVX_SCORE_PROJ, U><<<blocks, 256, 0, st>>>(
+        score_kernel<DT, KVX_SCORE_PROJ, U><<<blocks, KVX_SCORE_BLOCK, 0, st>>>(
             (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, (float)sign, s_new);
     return check_launch("qf_score_keys");
 }
@@ -515,14 +572,14 @@ int launch_gather(const void *k_kept, const void *v_kept, const float *s_kept, c
                   const void *k_new, const void *v_new, const float *s_new, int32_t pos_base,
                   const int32_t *keep_idx, int64_t G, int n_kept, int S, int budget, int j0, int n_out,
                   void *k_out, void *v_out, float *s_out, int32_t *pos_out, hipStream_t st) {
-    constexpr int U = 4;
-    constexpr int kRowsPerBlock = (256 / Row<DT>::kLanes) * U;
+    constexpr int U = KVX_GATHER_U;
+    constexpr int kRowsPerBlock = (KVX_GATHER_BLOCK / Row<DT>::kLanes) * U;
     const int rows = n_out - j0;
     if (rows <= 0 || G == 0) return KVX_OK;
     const int bpg = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     const int64_t blocks = G * bpg;
     if (blocks > INT32_MAX) return set_error(KVX_ERANGE, "kv_compact_gather: grid too large");
-    gather_kernel<DT, U><<<(uint32_t)blocks, 256, 0, st>>>(
+    gather_kernel<DT, U><<<(uint32_t)blocks, KVX_GATHER_BLOCK, 0, st>>>(
         (const char *)k_kept, (const char *)v_kept, s_kept, pos_kept, (const char *)k_new,
         (const char *)v_new, s_new, pos_base, keep_idx, n_kept, S, budget, j0, n_out, bpg,
         (char *)k_out, (char *)v_out, s_out, pos_out);
@@ -585,16 +642,22 @@ KVX_API int kv_evict_topk(const float *s_kept, const float *s_new, kvx_shape sha
     const int a = (int)n_kept, b = (int)S, bud = (int)p.budget, ns = (int)p.n_sink, rc2 = (int)p.recent;
     const int kl = p.keep == KVX_KEEP_LOW;
     const uint32_t grid = (uint32_t)G;
-    if (n_total <= 1024)
-        select_kernel<1><<<grid, 1024, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-    else if (n_total <= 2048)
-        select_kernel<2><<<grid, 1024, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-    else if (n_total <= 4096)
-        select_kernel<4><<<grid, 1024, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-    else if (n_total <= 8192)
-        select_kernel<8><<<grid, 1024, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    constexpr int NT = KVX_SELECT_NT;
+    static_assert(NT == 256 || NT == 512 || NT == 1024, "selection block size");
+    if (n_total <= NT)
+        select_kernel<1, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    else if (n_total <= 2 * NT)
+        select_kernel<2, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    else if (n_total <= 4 * NT)
+        select_kernel<4, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    else if (n_total <= 8 * NT)
+        select_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    else if (n_total <= 16 * NT)
+        select_kernel<16, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    else if (n_total <= 32 * NT)
+        select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
     else
-        select_kernel<16><<<grid, 1024, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        select_kernel<64, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
     return check_launch("kv_evict_topk");
 }
 

@@ -189,9 +189,13 @@ def decode_block(cfg: Config, g: int) -> Tuple[np.ndarray, np.ndarray]:
     return _encode(cfg, _keys_f32(cfg, g, 1, 256)), _encode(cfg, _values_f32(cfg, g, 1, 256))
 
 
-def batch_chunk(cfg: Config, groups: Sequence[int], chunk: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Stacked exact host bytes [len(groups), S, D] for one chunk."""
-    ks, vs = zip(*(group_chunk(cfg, g, chunk) for g in groups))
+def batch_chunk(cfg: Config, groups: Sequence[int], chunk: int, workers: int = 16) -> Tuple[np.ndarray, np.ndarray]:
+    """Stacked exact host bytes [len(groups), S, D] for one chunk (groups drawn on
+    a thread pool; every group has its own generator, so the bytes do not depend
+    on the pool)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max(1, min(workers, len(groups)))) as ex:
+        ks, vs = zip(*ex.map(lambda g: group_chunk(cfg, g, chunk), groups))
     return np.stack(ks), np.stack(vs)
 
 
