@@ -1,24 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the query-free KV-cache eviction step on one MI355X.
 
-Workload (one step): the chunked long prefill of 28 layers x 8 KV heads
-(224 groups), head_dim 128, bf16 K/V, 32768 tokens absorbed in 4096-token
-chunks into a cache of budget 4096 with 4 sinks, once with the L2-norm scorer
-(keep lowest) and once with the Q-Filters projection scorer on the planted
-direction with sign -1.  Each chunk is one score + select + compact pass over
-all 224 groups.  Inputs are seeded synthetic tensors resident in HBM before the
-timed region; the step starts from an empty cache each time.
+Default workload (one step): the chunked long prefill of 28 layers x 8 KV heads
+(224 groups), head_dim 128, bf16 K/V, 32768 tokens absorbed in 4096-token chunks
+into a cache of budget 4096 with 4 sinks, once with the L2-norm scorer (keep
+lowest) and once with the Q-Filters projection scorer on the planted direction
+with sign -1.  Each chunk is one score + select + compact pass over all groups.
+Inputs are seeded synthetic tensors resident in HBM before the timed region; the
+step starts from an empty cache each time.
+
+Other workloads (--workload): c2 (one 4096-token block, budget 512,
+projection), c3 (7168 groups, a full cache of budget 2048, then 256
+single-token decode steps with a recent window of 512; the cache is restored
+from a device snapshot, untimed, before each step), c5 (256 groups, 131072
+tokens in 8192-token chunks, budget 8192, key-SVD fallback filters estimated
+before the timed region).
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
-  value       tokens absorbed per second, summed over the two scorer runs
-  roofline    the compaction (gather) kernel of the evicting calls: algorithmic
-              bytes per launch / its mean duration from HIP events recorded on the
-              launch stream inside the timed region, against 8 TB/s
+  value        tokens absorbed per second over the whole step (all runs)
+  roofline     the dominant kernel (the compaction of evicting calls for
+               prefill, the in-place decode kernel for c3): algorithmic bytes
+               per launch over its mean duration from HIP events recorded on the
+               launch stream around every call, in a second timed pass
   cpu_baseline the oracle (plain C, OpenMP) on a sample of the same workload
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,113 +39,257 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 D = 128
+ROW = D * 2  # bytes of one bf16 K or V row
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_token_amd", "csrc", "kvx_device.hip")
-# HBM bytes per evicting compaction launch, from the two rocprofv3 counter runs
-# (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, factors from a 1 GiB device copy) in
-# profiles/c4_chunked_prefill_32k_hbm_counters.md, valid only for the kernel
-# source they were taken on.
-MEASURED_TRAFFIC = {"kernel_src_sha256_16": "fcba0c27a0cb1391", "bytes_per_launch": 977377568}
+# Calibrated HBM bytes per launch of the dominant kernel, from the two rocprofv3
+# counter runs (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; factors from a 1 GiB device
+# copy) summarised in profiles/, valid only for the kernel source they were
+# taken on (sha256 prefix of kvx_device.hip).
+MEASURED_TRAFFIC = {
+    "c4": {"kernel_src_sha256_16": "15d51da6eccb5151", "bytes_per_launch": 977357647},
+    "c3": {"kernel_src_sha256_16": "15d51da6eccb5151", "bytes_per_launch": 9141863511},
+}
+DESCRIPTIONS = {
+    "c2": "c2_qfilters_calibrated: 28 layers x 8 KV heads x 128 (224 groups), bf16, one 4096-token block, "
+          "budget 512, 4 sinks; projection on the planted filter, sign +1",
+    "c3": "c3_decode_stream: 32 sequences x 28 layers x 8 KV heads x 128 (7168 groups), bf16, cache full at "
+          "budget 2048, then 256 single-token steps; L2 keep-low, 4 sinks, recent 512",
+    "c4": "c4_chunked_prefill_32k: 28 layers x 8 KV heads x head_dim 128 (224 groups), bf16, 32768 tokens in "
+          "4096-token chunks, budget 4096, 4 sinks, recent 0; L2-norm keep-low run + Q-Filters (planted filter, "
+          "sign -1) run",
+    "c5": "c5_keysvd_fallback_128k: 32 layers x 8 KV heads x 128 (256 groups), bf16, 131072 tokens in 8192-token "
+          "chunks, budget 8192, 4 sinks; projection on key-SVD fallback filters (first 128 keys, estimated "
+          "before timing), sign +1",
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_workload(torch, stream):
-    from kv_cache_token_amd import synth
-    from kv_cache_token_amd.cache import EvictingCache
-    cfg = synth.CONFIGS[4]
-    with torch.cuda.stream(stream):
-        mus = synth.device_mus(cfg)
-        blocks = [synth.fill_device(cfg, S, 1000 + c, mus=mus) for c, S in enumerate(cfg.chunks)]
-        f = torch.from_numpy(synth.filters_mu(cfg)).cuda()
-        caches = []
-        for sc in cfg.scorers:
+class Workload:
+    """One plan per scorer run over HBM-resident seeded inputs."""
+
+    def __init__(self, torch, name, streams):
+        from kv_cache_token_amd import synth
+        from kv_cache_token_amd.cache import EvictingCache
+        cid = int(name[1:])
+        self.name, self.cfg, self.streams = name, synth.CONFIGS[cid], streams
+        cfg = self.cfg
+        with torch.cuda.stream(streams[0]):
+            mus = synth.device_mus(cfg) if cfg.keys == "aniso" else None
+            if cid == 3:
+                prefill = synth.fill_device(cfg, cfg.chunks[0], 3000)
+                kd, vd = synth.fill_device(cfg, 256, 3001)
+                kd, vd = kd.transpose(0, 1).contiguous(), vd.transpose(0, 1).contiguous()
+                self.blocks = [(kd[t].unsqueeze(1), vd[t].unsqueeze(1)) for t in range(256)]
+            else:
+                self.blocks = [synth.fill_device(cfg, S, 1000 * cid + c, mus=mus) for c, S in enumerate(cfg.chunks)]
+            f_mu = torch.from_numpy(synth.filters_mu(cfg)).cuda() if cfg.keys == "aniso" else None
+        self.caches, self.plans, self.snapshots = [], [], []
+        for i, sc in enumerate(cfg.scorers):
+            st = streams[i % len(streams)]
             keep = sc.keep if sc.mode == "l2" else "high"
-            caches.append(EvictingCache(cfg.L, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode,
-                                        f if sc.mode == "proj" else None, sc.sign, cfg.dtype, stream=stream))
-        plans = [c.plan(blocks) for c in caches]
-    torch.cuda.synchronize()
-    return cfg, blocks, caches, plans
+            c = EvictingCache(cfg.L, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode,
+                              f_mu if sc.filt == "mu" else None, sc.sign, cfg.dtype, stream=st,
+                              calib_tokens=cfg.calib_tokens)
+            with torch.cuda.stream(st):
+                if sc.filt == "keysvd":       # freeze the fallback filters once, outside the timed step
+                    c.update(*self.blocks[0])
+                    c.reset(keep_filters=True)
+                if cid == 3:                  # the decode step starts from a full cache
+                    c.update(*prefill)
+                    self.snapshots.append([x.clone() for x in c.buffers()])
+                    self.plans.append(c.plan(self.blocks, keep_state=True))
+                else:
+                    self.plans.append(c.plan(self.blocks))
+            self.caches.append(c)
+        torch.cuda.synchronize()
+        self.tokens_per_step = len(cfg.scorers) * cfg.B * sum(b[0].shape[1] for b in self.blocks)
+        self.dominant = "kv_evict_one_inplace" if cid == 3 else "kv_compact_gather"
+
+    def restore(self):
+        """Put back the cache contents the plans start from (untimed)."""
+        for c, snap in zip(self.caches, self.snapshots):
+            with self._torch.cuda.stream(c.stream):
+                for d, s in zip(c.buffers(), snap):
+                    d.copy_(s)
+
+    @property
+    def _torch(self):
+        import torch
+        return torch
+
+    def step(self, hook=None):
+        for p in self.plans:
+            p.run(hook)
 
 
-def algorithmic_bytes(torch, cfg, caches, plans, stream):
-    """Run each plan once call by call, reading keep_idx after every selection,
-    and count the bytes the method must move (per the workload's own survivors):
-    per group and call, S*Row (read incoming K) + 4*n_kept (stored scores)
-    + m_k*2*(2*Row+8) (kept survivors whose row changes: read and write K, V,
-    score, position) + m_n*(3*Row+8) (incoming survivors: read V, write K, V,
-    score, position).  Also the gather kernel's own bytes per evicting launch:
-    every output row reads K, V, score and its index and writes K, V, score and
-    position: 4*Row+16 bytes."""
-    row = D * 2
-    step_bytes = 0
-    gather_bytes = []
-    for cache, plan in zip(caches, plans):
-        state = {"n_kept": 0}
-        S_of = list(cfg.chunks)
-        call_chunk = []
-        c = -1
-        for name in plan.names:
+def algorithmic_bytes(torch, wl):
+    """Run each plan once call by call and count the bytes the method must
+    move, per group and call: S*Row (read incoming K) + 4*n_kept (stored
+    scores) + m_k*2*(2*Row+8) (kept survivors whose row changes: read and write
+    K, V, score, position) + m_n*(3*Row+8) (incoming survivors: read V, write
+    K, V, score, position).  Also the dominant kernel's own bytes per launch:
+    compaction of an evicting call = every output row reads K, V, score and
+    index and writes K, V, score and position (4*Row+16); decode = each moved
+    row read and written (2*(2*Row+8)), the candidate scores read (4 B each),
+    the incoming row read and written (2*Row+4 + 2*Row+8)."""
+    total, dom = 0, []
+    wl.restore()
+    for cache, plan in zip(wl.caches, wl.plans):
+        st = {"n_kept": plan.start[0], "S": 0, "pos": None}
+        G = cache.G
+
+        def hook(i, name, when, cache=cache, st=st):
+            nonlocal total
             if name == "qf_score_keys":
-                c += 1
-            call_chunk.append(c)
-
-        def hook(i, name, when, cache=cache, state=state):
-            nonlocal step_bytes
-            if when != "after":
+                if when == "after":
+                    st["S"] = cache.last_scores().shape[1]
                 return
-            ch = call_chunk[i]
-            S = S_of[ch]
-            nk = state["n_kept"]
-            if name == "kv_compact_gather":
-                G = cache.G
-                if nk + S <= cache.budget:        # append in place
-                    m_k, m_n = 0, S
-                    step_bytes += G * (S * row + 4 * nk + m_n * (3 * row + 8))
+            S, nk = st["S"], st["n_kept"]
+            if name == "kv_evict_one_inplace":
+                if when == "before":
+                    torch.cuda.synchronize()
+                    st["pos"] = cache.buffers()[3].clone()
+                    return
+                torch.cuda.synchronize()
+                if nk < cache.budget:
+                    total += G * (ROW + 4 * nk + (3 * ROW + 8))
+                    dom.append(G * (4 * ROW + 12))
+                else:
+                    diff = st["pos"] != cache.buffers()[3]
+                    changed = diff.any(dim=1)
+                    first = diff.to(torch.int32).argmax(dim=1).to(torch.int64)
+                    victim = torch.where(changed, first, torch.full_like(first, cache.budget))
+                    m_k = int((cache.budget - 1 - victim).clamp(min=0).sum())
+                    m_n = int(changed.sum())
+                    total += G * (ROW + 4 * nk) + m_k * 2 * (2 * ROW + 8) + m_n * (3 * ROW + 8)
+                    cands = cache.budget + 1 - cache.recent - cache.n_sink
+                    dom.append(m_k * 2 * (2 * ROW + 8) + G * 4 * cands + m_n * (4 * ROW + 12))
+                st["n_kept"] = min(nk + 1, cache.budget)
+            elif name == "kv_compact_gather" and when == "after":
+                if nk + S <= cache.budget:
+                    total += G * (S * ROW + 4 * nk + S * (3 * ROW + 8))
                 else:
                     torch.cuda.synchronize()
                     idx = cache.keep_idx.to(torch.int64)
                     j = torch.arange(idx.shape[1], device=idx.device)[None, :]
                     m_k = int(((idx < nk) & (idx != j)).sum())
                     m_n = int((idx >= nk).sum())
-                    step_bytes += G * (S * row + 4 * nk) + m_k * 2 * (2 * row + 8) + m_n * (3 * row + 8)
-                    gather_bytes.append(G * cache.budget * (4 * row + 16))
-                state["n_kept"] = min(nk + S, cache.budget)
+                    total += G * (S * ROW + 4 * nk) + m_k * 2 * (2 * ROW + 8) + m_n * (3 * ROW + 8)
+                    dom.append(G * cache.budget * (4 * ROW + 16))
+                st["n_kept"] = min(nk + S, cache.budget)
 
-        with torch.cuda.stream(stream):
+        with torch.cuda.stream(cache.stream):
             plan.run(hook)
         torch.cuda.synchronize()
-    return step_bytes, gather_bytes
+    return total, dom
 
 
-def cpu_baseline(cfg, n_groups):
+def timed_steps(torch, wl, n):
+    """Mean milliseconds per step over n steps.  Without snapshots the steps run
+    back to back between two events; with snapshots every step is bracketed by
+    its own events and the untimed restore runs between them."""
+    ev = torch.cuda.Event
+    s0, rest = wl.streams[0], wl.streams[1:]
+
+    def bracket(k):
+        start, end = ev(enable_timing=True), ev(enable_timing=True)
+        start.record(s0)
+        for s in rest:
+            s.wait_event(start)
+        with torch.cuda.stream(s0):
+            for _ in range(k):
+                wl.step()
+        for s in rest:
+            j = ev()
+            j.record(s)
+            s0.wait_event(j)
+        end.record(s0)
+        return start, end
+
+    if not wl.snapshots:
+        start, end = bracket(n)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n
+    total = 0.0
+    for _ in range(n):
+        wl.restore()
+        torch.cuda.synchronize()
+        start, end = bracket(1)
+        torch.cuda.synchronize()
+        total += start.elapsed_time(end)
+    return total / n
+
+
+def kernel_times(torch, wl, steps):
+    """Second timed pass, one plan at a time: an event pair on the plan's own
+    stream around every library call."""
+    per = {}
+    ev = torch.cuda.Event
+    for _ in range(steps):
+        wl.restore()
+        torch.cuda.synchronize()
+        for p in wl.plans:
+            rec = []
+
+            def hook(i, name, when, p=p, rec=rec):
+                e = ev(enable_timing=True)
+                e.record(p.cache.stream)
+                rec.append((name, when, e))
+
+            p.run(hook)
+            torch.cuda.synchronize()
+            for k in range(0, len(rec), 2):
+                (n0, w0, e0), (n1, w1, e1) = rec[k], rec[k + 1]
+                assert w0 == "before" and w1 == "after" and n0 == n1
+                per.setdefault(n0, []).append(e0.elapsed_time(e1))
+    return per
+
+
+def cpu_baseline(wl, n_groups):
     """The oracle as it stands, on a sample of the same workload (exact seeded
-    host bytes of n_groups groups, both scorer runs over the whole stream)."""
+    host bytes of a sample of groups, every run of the step)."""
     import numpy as np
 
     import oracle
     from kv_cache_token_amd import synth
+    from oracle import calib
+    cfg = wl.cfg
     sample = synth.sample_groups(cfg, n_groups)
     t0 = time.perf_counter()
-    chunks = [synth.batch_chunk(cfg, sample, c) for c in range(len(cfg.chunks))]
+    if cfg.cid == 3:
+        pre = synth.batch_chunk(cfg, sample, 0)
+        dec = [synth.decode_block(cfg, g) for g in sample]
+        chunks = [(np.stack([d[0][t:t + 1] for d in dec]), np.stack([d[1][t:t + 1] for d in dec]))
+                  for t in range(256)]
+    else:
+        chunks = [synth.batch_chunk(cfg, sample, c) for c in range(len(cfg.chunks))]
     log("cpu baseline: generated %d groups in %.1f s" % (len(sample), time.perf_counter() - t0))
-    f_lh = synth.filters_mu(cfg)
-    fs = np.stack([f_lh[cfg.group_lbh(g)[0], cfg.group_lbh(g)[2]] for g in sample])
     caches = []
     for sc in cfg.scorers:
         keep = sc.keep if sc.mode == "l2" else "high"
-        caches.append(oracle.OracleCache(len(sample), D, cfg.dtype, cfg.budget, cfg.n_sink, cfg.recent, keep,
-                                         sc.mode, fs if sc.mode == "proj" else None, sc.sign))
+        fs = None
+        if sc.filt == "mu":
+            f_lh = synth.filters_mu(cfg)
+            fs = np.stack([f_lh[cfg.group_lbh(g)[0], cfg.group_lbh(g)[2]] for g in sample])
+        elif sc.filt == "keysvd":
+            k0 = synth.bf16_bits_to_f32(chunks[0][0][:, :cfg.calib_tokens]).astype(np.float64)
+            fs = np.stack([calib.estimate_filter_dir(k0[i]) for i in range(len(sample))]).astype(np.float32)
+        oc = oracle.OracleCache(len(sample), D, cfg.dtype, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode,
+                                fs, sc.sign)
+        if cfg.cid == 3:
+            oc.update(*pre)               # the decode step starts from a full cache (untimed)
+        caches.append(oc)
     t0 = time.perf_counter()
     for oc in caches:
         for K, V in chunks:
             oc.update(K, V)
     t = time.perf_counter() - t0
-    tokens = len(cfg.scorers) * cfg.tokens * len(sample) / cfg.G     # workload-equivalent tokens
-    return {"value": tokens / t, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d groups, both scorer runs over the full %d-token stream (%.2f s)"
-                      % (len(sample), cfg.G, cfg.tokens, t)}
+    tokens = wl.tokens_per_step * len(sample) / cfg.G      # workload-equivalent tokens
+    return {"value": round(tokens / t, 1), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d groups, every run of the step (%.2f s of oracle time)" % (len(sample), cfg.G, t)}
 
 
 def main():
@@ -144,9 +297,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
+                    help="run the step's independent scorer runs on this many streams")
     ap.add_argument("--cpu-groups", type=int, default=32, help="groups in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true", help="replay each step as one captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for byte counters)")
     args = ap.parse_args()
@@ -160,106 +315,64 @@ def main():
     _lib.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev_name = torch.cuda.get_device_name(0)
-    stream = torch.cuda.Stream()
-    cfg, blocks, caches, plans = build_workload(torch, stream)
-    log("workload ready on %s: %d groups, %d chunks of %d" % (dev_name, cfg.G, len(cfg.chunks), cfg.chunks[0]))
+    streams = [torch.cuda.Stream() for _ in range(args.streams)]
+    wl = Workload(torch, args.workload, streams)
+    cfg = wl.cfg
+    log("workload %s ready on %s: %d groups, %d calls per run" % (args.workload, dev_name, cfg.G, len(wl.blocks)))
 
     if args.copy_calibration:
-        with torch.cuda.stream(stream):
+        with torch.cuda.stream(streams[0]):
             src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
             dst = torch.empty_like(src)
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
 
-    step_bytes, gather_bytes = algorithmic_bytes(torch, cfg, caches, plans, stream)
-    log("algorithmic bytes per step: %.3f GB; gather launches per step: %d" % (step_bytes / 1e9, len(gather_bytes)))
+    step_bytes, dom_bytes = algorithmic_bytes(torch, wl)
+    log("algorithmic bytes per step: %.3f GB" % (step_bytes / 1e9))
+    if args.warmup:
+        timed_steps(torch, wl, args.warmup)
+    ms_per_step = timed_steps(torch, wl, args.steps)
 
-    def step(hook=None):
-        for p in plans:
-            p.run(hook)
-
-    graph = None
-    if args.graph:
-        with torch.cuda.stream(stream):
-            step()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            step()
-        torch.cuda.synchronize()
-
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            graph.replay() if graph else step()
-    torch.cuda.synchronize()
-
-    # Timed region: K steps; the compaction launches of evicting calls are
-    # bracketed by events on the launch stream.
-    gather_events = []
-    ev = torch.cuda.Event
-
-    def hook(i, name, when):
-        if name != "kv_compact_gather":
-            return
-        e = ev(enable_timing=True)
-        e.record(stream)
-        gather_events.append((i, when, e))
-
-    start, end = ev(enable_timing=True), ev(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    with torch.cuda.stream(stream):
-        for _ in range(args.steps):
-            if graph:
-                graph.replay()
-            else:
-                step(hook)
-    end.record(stream)
-    end.synchronize()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-
-    # per-launch gather durations (evicting calls only: every call after the first chunk)
-    gather_ms = []
-    if gather_events:
-        for k in range(0, len(gather_events), 2):
-            (i0, w0, e0), (i1, w1, e1) = gather_events[k], gather_events[k + 1]
-            assert w0 == "before" and w1 == "after" and i0 == i1
-            gather_ms.append((i0, e0.elapsed_time(e1)))
-    evict_ms = [ms for n, (i, ms) in enumerate(gather_ms) if (n % len(cfg.chunks)) != 0]
-    roof = None
-    if evict_ms:
-        mean_ms = sum(evict_ms) / len(evict_ms)
-        bytes_per_launch = sum(gather_bytes) / len(gather_bytes)
-        achieved = bytes_per_launch / (mean_ms * 1e-3) / 1e9
-        import hashlib
-        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-        traffic = MEASURED_TRAFFIC["bytes_per_launch"] if sha == MEASURED_TRAFFIC["kernel_src_sha256_16"] else None
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic, "traffic_unit": "bytes/launch",
-                "kernel": "kv_compact_gather (evicting calls)", "launches": len(evict_ms),
-                "mean_launch_us": round(mean_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(bytes_per_launch)}
-    tokens_per_step = len(cfg.scorers) * cfg.tokens
-    value = tokens_per_step / (ms_per_step * 1e-3)
+    per = kernel_times(torch, wl, args.steps)
+    breakdown = {n: {"launches_per_step": len(v) // args.steps, "mean_us": round(1e3 * sum(v) / len(v), 2)}
+                 for n, v in per.items()}
+    dom_ms = per[wl.dominant]
+    if wl.dominant == "kv_compact_gather":
+        # evicting launches only: the leading calls of each run that only append are left out
+        calls_per_run = len(dom_ms) // (args.steps * len(wl.plans))
+        n_append = calls_per_run - len(dom_bytes) // len(wl.plans)
+        dom_ms = [x for n, x in enumerate(dom_ms) if n % calls_per_run >= n_append]
+    mean_ms = sum(dom_ms) / len(dom_ms)
+    bytes_per_launch = sum(dom_bytes) / len(dom_bytes)
+    achieved = bytes_per_launch / (mean_ms * 1e-3) / 1e9
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    mt = MEASURED_TRAFFIC.get(args.workload)
+    traffic = mt["bytes_per_launch"] if mt and sha == mt["kernel_src_sha256_16"] else None
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic, "traffic_unit": "bytes/launch",
+            "kernel": wl.dominant + (" (evicting calls)" if wl.dominant == "kv_compact_gather" else ""),
+            "launches": len(dom_ms), "mean_launch_us": round(mean_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+    value = wl.tokens_per_step / (ms_per_step * 1e-3)
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": "evicted-cache tokens/sec (score+select+compact), achieved HBM GB/s vs peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded anisotropic keys drift*mu + N(0,0.25), V ~ N(0,1); HBM-resident)",
-        "config": {"workload": "c4_chunked_prefill_32k: 28 layers x 8 KV heads x head_dim 128 (224 groups), bf16, "
-                               "32768 tokens in 4096-token chunks, budget 4096, 4 sinks, recent 0; "
-                               "L2-norm keep-low run + Q-Filters (planted filter, sign -1) run",
-                   "groups": cfg.G, "tokens_per_run": cfg.tokens, "chunk": cfg.chunks[0], "budget": cfg.budget,
-                   "runs_per_step": len(cfg.scorers), "graph": bool(graph), "device": dev_name},
+        "dtype": "bf16",
+        "data": "synthetic (seeded, HBM-resident; keys %s, V ~ N(0,1))" % {
+            "aniso": "drift*mu + N(0,0.25)", "lognorm": "r*u, ln r ~ N(0,0.25)", "gauss": "N(0,1)"}[cfg.keys],
+        "config": {"workload": DESCRIPTIONS[args.workload], "groups": cfg.G,
+                   "tokens_per_step": wl.tokens_per_step, "runs_per_step": len(wl.plans),
+                   "budget": cfg.budget, "streams": args.streams, "device": dev_name},
         "step_algorithmic_GBps": round(step_gbps, 1), "step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
         "step_algorithmic_bytes": int(step_bytes),
         "roofline": roof,
+        "kernels": breakdown,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_groups)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_groups)
     print(json.dumps(out), flush=True)
 
 

@@ -106,10 +106,12 @@ class EvictingCache:
         """Scores [G, S] the last update computed for its incoming rows."""
         return self._s_new
 
-    def reset(self) -> None:
+    def reset(self, keep_filters: bool = False) -> None:
+        """Empty the cache.  Fallback filters (estimated from the stream's first
+        keys) are forgotten unless keep_filters is set."""
         self.n_kept = 0
         self.tokens_seen = 0
-        if self.mode == "proj" and self.calib_tokens > 0 and self.score_shape is not self.shape:
+        if not keep_filters and self.mode == "proj" and self.calib_tokens > 0 and self.score_shape is not self.shape:
             self.filters = None
 
     def stats(self) -> dict:
@@ -160,37 +162,41 @@ class EvictingCache:
         self.tokens_seen += S
         return calls, (k_new, v_new, s_new)
 
-    def plan(self, blocks) -> "StreamPlan":
+    def plan(self, blocks, keep_state: bool = False) -> "StreamPlan":
         """Validate and record, once, the library calls that absorb `blocks`
-        (a list of (K, V) device tensors) into an empty cache.  The plan replays
-        them with no per-call marshalling (or inside a captured HIP graph); it
-        keeps the tensors it points at alive.  The cache is left empty."""
-        self.n_kept, self.tokens_seen, self._cur = 0, 0, 0
+        (a list of (K, V) device tensors) into an empty cache, or, with
+        keep_state, into the cache as it stands (the caller then restores the
+        buffers before each replay).  The plan replays the calls with no
+        per-call marshalling (or inside a captured HIP graph) and keeps the
+        tensors it points at alive.  The cache's bookkeeping is left at the
+        plan's starting state."""
+        start = (self.n_kept, self.tokens_seen, self._cur) if keep_state else (0, 0, 0)
+        self.n_kept, self.tokens_seen, self._cur = start
         calls, keep = [], []
         for k, v in blocks:
             c, refs = self._step(k, v, prepare=True)
             calls += c
             keep.append(refs)
         final = (self.n_kept, self.tokens_seen, self._cur)
-        self.n_kept, self.tokens_seen, self._cur = 0, 0, 0
-        return StreamPlan(self, calls, final, keep)
+        self.n_kept, self.tokens_seen, self._cur = start
+        return StreamPlan(self, calls, start, final, keep)
 
 
 class StreamPlan:
     """Prepared library calls of a whole block stream (see EvictingCache.plan)."""
 
-    def __init__(self, cache: EvictingCache, calls, final, keepalive):
-        self.cache, self.calls, self.final, self._keep = cache, calls, final, keepalive
+    def __init__(self, cache: EvictingCache, calls, start, final, keepalive):
+        self.cache, self.calls, self.start, self.final, self._keep = cache, calls, start, final, keepalive
 
     @property
     def names(self):
         return [f.__name__ for f, _ in self.calls]
 
     def run(self, hook=None) -> None:
-        """Enqueue every call, starting from an empty cache; hook(i, name, when)
+        """Enqueue every call from the plan's starting state; hook(i, name, when)
         with when in ("before", "after") is called around each call."""
         c = self.cache
-        c.n_kept, c.tokens_seen, c._cur = 0, 0, 0
+        c.n_kept, c.tokens_seen, c._cur = self.start
         for i, (f, args) in enumerate(self.calls):
             if hook:
                 hook(i, f.__name__, "before")

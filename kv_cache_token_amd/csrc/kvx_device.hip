@@ -31,9 +31,6 @@ struct Row {
 #ifndef KVX_SCORE_U
 #define KVX_SCORE_U 4
 #endif
-#ifndef KVX_SCORE_BLOCKS_PER_CU
-#define KVX_SCORE_BLOCKS_PER_CU 0  // 0: one block per row tile, no grid-stride cap
-#endif
 #ifndef KVX_GATHER_U
 #define KVX_GATHER_U 1
 #endif
@@ -55,7 +52,13 @@ struct Row {
 #define KVX_GATHER_NT_STORE 1
 #endif
 #ifndef KVX_DECODE_NT
-#define KVX_DECODE_NT 0
+#define KVX_DECODE_NT 1
+#endif
+#ifndef KVX_DECODE_U
+#define KVX_DECODE_U 8
+#endif
+#ifndef KVX_DECODE_BLOCK
+#define KVX_DECODE_BLOCK 512
 #endif
 #ifndef KVX_SELECT_NT
 #define KVX_SELECT_NT 1024
@@ -109,83 +112,142 @@ __device__ __forceinline__ uint32_t select_key(float s, int keep_low) {
 }
 
 // ---------------------------------------------------------------------------
-// Step 1: score kernel.  Kernel rows are [n_rows, D] contiguous (n_rows = G*S).
-// A row is read by kLanes lanes, 16 bytes each (bf16: 16 lanes, 4 rows per
-// wave per load).  Each lane sums its elements in order with fused
-// multiply-adds, then the row's lanes combine by an xor butterfly; the order is
-// a function of the row alone, so a row's score does not depend on S, on the
-// tile it falls in or on the grid.
+// Step 1: scoring.  A row is read by kLanes lanes, 16 bytes each (bf16: 16
+// lanes, 4 rows per wave per load).  Each lane sums its elements in order with
+// fused multiply-adds and the row's lanes combine by an xor butterfly; that
+// order is a function of the row alone, so a row's score does not depend on S,
+// on the tile it falls in or on the grid.  A lane always covers the same slice
+// of the head dim, so its slice of the group's filter stays in registers.
 // ---------------------------------------------------------------------------
+template <int DT, int MODE>
+__device__ __forceinline__ float row_partial(uint4 raw, const float *f) {
+    using R = Row<DT>;
+    float x[R::kElemsPerLane];
+    widen<DT>(raw, x);
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < R::kElemsPerLane; ++e)
+        acc = MODE == KVX_SCORE_L2 ? __builtin_fmaf(x[e], x[e], acc) : __builtin_fmaf(x[e], f[e], acc);
+#pragma unroll
+    for (int off = R::kLanes / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    return acc;
+}
+
+template <int DT>
+__device__ __forceinline__ void load_filter_slice(const float *__restrict__ filt, uint32_t l, uint32_t h,
+                                                  uint32_t H, uint32_t part, float *f) {
+    using R = Row<DT>;
+    const float4 *f4 = reinterpret_cast<const float4 *>(filt + (size_t)(l * H + h) * kD + part * R::kElemsPerLane);
+#pragma unroll
+    for (int q = 0; q < R::kElemsPerLane / 4; ++q) {
+        const float4 v = f4[q];
+        f[4 * q] = v.x;
+        f[4 * q + 1] = v.y;
+        f[4 * q + 2] = v.z;
+        f[4 * q + 3] = v.w;
+    }
+}
+
+__device__ __forceinline__ float finish_score(int mode, float acc, float sign) {
+    const float s = mode == KVX_SCORE_L2 ? __builtin_sqrtf(acc) : sign * acc;
+    return s + 0.0f;  // -0 -> +0
+}
+
+// Group-major tiles: block b scores rows [tile*RPB, tile*RPB + RPB) of group
+// b / tiles (used when a group has at least a tile of rows).
 template <int DT, int MODE, int U>
-__global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_kernel(const char *__restrict__ k, uint32_t n_rows,
-                                                    uint32_t S, uint32_t BH, uint32_t H,
-                                                    const float *__restrict__ filt, float sign,
-                                                    float *__restrict__ out) {
+__global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_tile_kernel(
+    const char *__restrict__ k, uint32_t S, uint32_t tiles, uint32_t BH, uint32_t H,
+    const float *__restrict__ filt, float sign, float *__restrict__ out) {
+    using R = Row<DT>;
+    constexpr int kRowsPerLoad = 64 / R::kLanes;
+    constexpr int kRowsPerWave = kRowsPerLoad * U;
+    const uint32_t g = blockIdx.x / tiles;
+    const uint32_t tile = blockIdx.x - g * tiles;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t sub = lane / R::kLanes, part = lane % R::kLanes;
+    const uint32_t r0 = tile * (KVX_SCORE_BLOCK / 64) * kRowsPerWave + (threadIdx.x >> 6) * kRowsPerWave;
+    const char *kg = k + (size_t)g * S * R::kBytes;
+    float f[R::kElemsPerLane];
+    if constexpr (MODE == KVX_SCORE_PROJ) load_filter_slice<DT>(filt, g / BH, g % H, H, part, f);
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t r = r0 + u * kRowsPerLoad + sub;
+        raw[u] = r < S ? ld16<KVX_SCORE_NT_LOAD>(kg + (size_t)r * R::kBytes + part * 16) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t r = r0 + u * kRowsPerLoad + sub;
+        const float acc = row_partial<DT, MODE>(raw[u], f);
+        if (part == 0 && r < S) out[(size_t)g * S + r] = finish_score(MODE, acc, sign);
+    }
+}
+
+// Flat rows (a group has fewer rows than a tile, e.g. one decode token): row r
+// belongs to group r / S.
+template <int DT, int MODE, int U>
+__global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_flat_kernel(
+    const char *__restrict__ k, uint32_t n_rows, uint32_t S, uint32_t BH, uint32_t H,
+    const float *__restrict__ filt, float sign, float *__restrict__ out) {
     using R = Row<DT>;
     constexpr int kRowsPerLoad = 64 / R::kLanes;
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t sub = lane / R::kLanes;
-    const uint32_t part = lane % R::kLanes;
+    const uint32_t sub = lane / R::kLanes, part = lane % R::kLanes;
     const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const uint32_t wave_stride = gridDim.x * (blockDim.x >> 6) * (kRowsPerLoad * U);
-    for (uint32_t row0 = wave * (kRowsPerLoad * U); row0 < n_rows; row0 += wave_stride) {
+    const uint32_t row0 = wave * (kRowsPerLoad * U);
     uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t r = row0 + u * kRowsPerLoad + sub;
-        raw[u] = r < n_rows ? ld16<KVX_SCORE_NT_LOAD>(k + (size_t)r * R::kBytes + part * 16)
-                            : make_uint4(0, 0, 0, 0);
+        raw[u] = r < n_rows ? ld16<KVX_SCORE_NT_LOAD>(k + (size_t)r * R::kBytes + part * 16) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t r = row0 + u * kRowsPerLoad + sub;
-        float x[R::kElemsPerLane];
-        widen<DT>(raw[u], x);
-        float acc = 0.0f;
-        if constexpr (MODE == KVX_SCORE_L2) {
-#pragma unroll
-            for (int e = 0; e < R::kElemsPerLane; ++e) acc = __builtin_fmaf(x[e], x[e], acc);
-        } else {
+        float f[R::kElemsPerLane];
+        if constexpr (MODE == KVX_SCORE_PROJ) {
             const uint32_t g = r < n_rows ? r / S : 0u;
-            const uint32_t l = g / BH, h = g % H;
-            const float4 *f4 = reinterpret_cast<const float4 *>(
-                filt + (size_t)(l * H + h) * kD + part * R::kElemsPerLane);
-            float f[R::kElemsPerLane];
-#pragma unroll
-            for (int q = 0; q < R::kElemsPerLane / 4; ++q) {
-                const float4 v = f4[q];
-                f[4 * q] = v.x;
-                f[4 * q + 1] = v.y;
-                f[4 * q + 2] = v.z;
-                f[4 * q + 3] = v.w;
-            }
-#pragma unroll
-            for (int e = 0; e < R::kElemsPerLane; ++e) acc = __builtin_fmaf(x[e], f[e], acc);
+            load_filter_slice<DT>(filt, g / BH, g % H, H, part, f);
         }
-#pragma unroll
-        for (int off = R::kLanes / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (part == 0 && r < n_rows) {
-            const float s = MODE == KVX_SCORE_L2 ? __builtin_sqrtf(acc) : sign * acc;
-            out[r] = s + 0.0f;  // -0 -> +0
-        }
+        const float acc = row_partial<DT, MODE>(raw[u], f);
+        if (part == 0 && r < n_rows) out[r] = finish_score(MODE, acc, sign);
     }
-    }
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide inclusive prefix sum on the DPP lane network (no LDS round trip):
+// Hillis-Steele inside each row of 16 lanes, then the row totals are carried
+// across rows with the row broadcasts.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
 }
 
 // ---------------------------------------------------------------------------
 // Steps 2-3: selection.  One workgroup of NT threads per group.  Thread t holds
 // the keys of rows t, t + NT, ... (M of them) in registers, so every load is
 // coalesced.  The budget-th largest key tau is found with four 8-bit radix
-// passes over an LDS histogram; then the kept rows are those with key > tau
-// plus the first `quota` rows (in row order) with key == tau, and their
-// indices are written in row order using per-64-row chunk counts.
-// Protected rows get key 0xFFFFFFFF, above every real score's key.
+// passes; each wave counts into its own LDS histogram (scores cluster, so a
+// shared histogram would serialise the waves on a few bins), the histograms of
+// the next pass are cleared while the current one is scanned, and one wave
+// sums the per-wave counts and scans them.  The kept rows are those with
+// key > tau plus the first `quota` rows (in row order) with key == tau; their
+// indices are written in row order using per-64-row chunk counts.  Protected
+// rows get key 0xFFFFFFFF, above every real score's key.
 // ---------------------------------------------------------------------------
 template <int M, int NT>
 __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_kept,
                                                       const float *__restrict__ s_new, int n_kept,
                                                       int S, int budget, int n_sink, int recent,
                                                       int keep_low, int32_t *__restrict__ keep_idx) {
+    constexpr int NW = NT / 64;
     const int g = blockIdx.x;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int n_total = n_kept + S;
@@ -196,6 +258,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
     }
     const float *sk = s_kept + (size_t)g * budget;
     const float *sn = s_new + (size_t)g * S;
+
+    __shared__ uint4 hist4[2][NW][64];  // per-wave 256-bin histograms, two passes' worth
+    __shared__ uint32_t sel[2];
+    __shared__ uint32_t chunk[KVX_MAX_TOTAL / 64];
+    uint32_t(*hist)[NW][256] = reinterpret_cast<uint32_t(*)[NW][256]>(hist4);
 
     uint32_t key[M];
 #pragma unroll
@@ -209,70 +276,72 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
         }
         key[i] = kk;
     }
-
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t sel[2];
-    __shared__ uint32_t chunk[KVX_MAX_TOTAL / 64];
+    for (int i = t; i < NW * 64; i += NT) (&hist4[0][0][0])[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
 
     uint32_t prefix = 0, pmask = 0, krem = (uint32_t)budget;
+#pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        if (t < 256) hist[t] = 0;
-        __syncthreads();
+        uint32_t *h = hist[pass & 1][w];
 #pragma unroll
         for (int i = 0; i < M; ++i) {
             const int r = i * NT + t;
             bool act = r < n_total && (key[i] & pmask) == prefix;
             const uint32_t d = (key[i] >> shift) & 0xFFu;
             // Wave-aggregated increments while the leading digit covers many
-            // lanes (scores cluster, so one digit often covers most of a wave);
-            // once the digits spread, one atomic per lane.
+            // lanes; once the digits spread, one atomic per lane.
             for (int it = 0; it < 4; ++it) {
                 const uint64_t am = __ballot(act);
                 if (am == 0) break;
                 const int leader = __ffsll((unsigned long long)am) - 1;
                 const uint32_t ld = __builtin_amdgcn_readlane(d, leader);
                 const bool mine = act && d == ld;
-                const uint64_t m = __ballot(mine);
-                const uint32_t cnt = (uint32_t)__popcll(m);
-                if (lane == leader) atomicAdd(&hist[ld], cnt);
+                const uint32_t cnt = (uint32_t)__popcll(__ballot(mine));
+                if (lane == leader) atomicAdd(&h[ld], cnt);
                 if (mine) act = false;
                 if (cnt < 8) break;
             }
-            if (act) atomicAdd(&hist[d], 1u);
+            if (act) atomicAdd(&h[d], 1u);
         }
         __syncthreads();
         if (w == 0) {
-            const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1];
-            const uint32_t c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
-            const uint32_t local = c0 + c1 + c2 + c3;
-            uint32_t incl = local;  // keys in this lane's bins or any higher bin
+            // lane l owns bins 255-4l (c0) down to 252-4l (c3): higher bins in lower lanes
+            uint4 c = make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t v = __shfl_down(incl, off);
-                if (lane + off < 64) incl += v;
+            for (int v = 0; v < NW; ++v) {
+                const uint4 x = hist4[pass & 1][v][63 - lane];
+                c.x += x.x;
+                c.y += x.y;
+                c.z += x.z;
+                c.w += x.w;
             }
+            const uint32_t c0 = c.w, c1 = c.z, c2 = c.y, c3 = c.x;
+            const uint32_t local = c0 + c1 + c2 + c3;
+            const uint32_t incl = wave_prefix_incl(local);  // keys in this lane's bins or higher ones
             const uint32_t above = incl - local;
             if (above < krem && krem <= incl) {
                 uint32_t cum = above, d, nk;
-                if (cum + c3 >= krem) {
-                    d = 4 * lane + 3;
+                if (cum + c0 >= krem) {
+                    d = 255 - 4 * lane;
                     nk = krem - cum;
-                } else if ((cum += c3) + c2 >= krem) {
-                    d = 4 * lane + 2;
+                } else if ((cum += c0) + c1 >= krem) {
+                    d = 254 - 4 * lane;
                     nk = krem - cum;
-                } else if ((cum += c2) + c1 >= krem) {
-                    d = 4 * lane + 1;
+                } else if ((cum += c1) + c2 >= krem) {
+                    d = 253 - 4 * lane;
                     nk = krem - cum;
                 } else {
-                    cum += c1;
-                    d = 4 * lane;
+                    cum += c2;
+                    d = 252 - 4 * lane;
                     nk = krem - cum;
                 }
                 sel[0] = d;
                 sel[1] = nk;
             }
         }
+        if (pass < 3)  // clear the other histograms for the next pass meanwhile
+            for (int i = t; i < NW * 64; i += NT) (&hist4[(pass + 1) & 1][0][0])[i] = make_uint4(0, 0, 0, 0);
         __syncthreads();
         prefix |= sel[0] << shift;
         pmask |= 0xFFu << shift;
@@ -285,7 +354,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
     const int nchunks = (n_total + 63) >> 6;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-        const int c = i * (NT / 64) + w;
+        const int c = i * NW + w;
         const int r = c * 64 + lane;
         const bool valid = r < n_total;
         const uint64_t gm = __ballot(valid && key[i] > tau);
@@ -302,13 +371,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
             a[j] = c < nchunks ? chunk[c] : 0u;
             local += a[j];
         }
-        uint32_t incl = local;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t v = __shfl_up(incl, off);
-            if (lane >= off) incl += v;
-        }
-        uint32_t run = incl - local;
+        uint32_t run = wave_prefix_incl(local) - local;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c = 4 * lane + j;
@@ -320,7 +383,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-        const int c = i * (NT / 64) + w;
+        const int c = i * NW + w;
         const int r = c * 64 + lane;
         const bool valid = r < n_total;
         const uint64_t gm = __ballot(valid && key[i] > tau);
@@ -409,15 +472,17 @@ __global__ __launch_bounds__(KVX_GATHER_BLOCK) void gather_kernel(
 // next chunk's sources, so chunk-by-chunk order makes the shift race-free.
 // ---------------------------------------------------------------------------
 template <int DT, int U>
-__global__ __launch_bounds__(256) void evict_one_kernel(
+__global__ __launch_bounds__(KVX_DECODE_BLOCK) void evict_one_kernel(
     char *__restrict__ k_cache, char *__restrict__ v_cache, float *__restrict__ s_cache,
     int32_t *__restrict__ pos_cache, const char *__restrict__ k_new, const char *__restrict__ v_new,
     const float *__restrict__ s_new, int32_t pos_base, int n_kept, int budget, int n_sink,
     int recent, int keep_low) {
     using R = Row<DT>;
     constexpr int kSlots = 2 * R::kLanes;          // K lanes then V lanes of one row
-    constexpr int kRowsPerPass = 256 / kSlots;
-    constexpr int C = kRowsPerPass * U;            // rows per chunk (<= 256)
+    constexpr int NB = KVX_DECODE_BLOCK;
+    constexpr int kRowsPerPass = NB / kSlots;
+    constexpr int C = kRowsPerPass * U;            // rows per chunk
+    static_assert(C <= NB, "one thread moves each chunk row's score and position");
     const int g = blockIdx.x;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     char *kc = k_cache + (size_t)g * budget * R::kBytes;
@@ -430,7 +495,7 @@ __global__ __launch_bounds__(256) void evict_one_kernel(
         const int n_total = budget + 1;
         const int lo = n_sink, hi = n_total - recent;
         uint64_t best = ~0ull;
-        for (int r = lo + t; r < hi; r += 256) {
+        for (int r = lo + t; r < hi; r += NB) {
             const float s = r < budget ? sc[r] : s_new[g];
             const uint64_t kk = ((uint64_t)select_key(s, keep_low) << 32) |
                                 (uint64_t)(0xFFFFFFFFu - (uint32_t)r);
@@ -443,12 +508,12 @@ __global__ __launch_bounds__(256) void evict_one_kernel(
             const uint64_t o = ((uint64_t)hi32 << 32) | lo32;
             best = o < best ? o : best;
         }
-        __shared__ uint64_t wbest[4];
+        __shared__ uint64_t wbest[NB / 64];
         if (lane == 0) wbest[w] = best;
         __syncthreads();
         best = wbest[0];
 #pragma unroll
-        for (int i = 1; i < 4; ++i) best = wbest[i] < best ? wbest[i] : best;
+        for (int i = 1; i < NB / 64; ++i) best = wbest[i] < best ? wbest[i] : best;
         const int victim = (int)(0xFFFFFFFFu - (uint32_t)best);
         if (victim >= budget) return;  // the incoming row is the one dropped
 
@@ -456,32 +521,74 @@ __global__ __launch_bounds__(256) void evict_one_kernel(
         const int half = slot / R::kLanes;  // 0: K, 1: V
         const int part = slot % R::kLanes;
         const int sub = t / kSlots;
-        char *base = half ? vc : kc;
-        for (int c0 = victim + 1; c0 < budget; c0 += C) {
+        char *base = (half ? vc : kc) + part * 16;
+        struct Chunk {
             uint4 d[U];
-            float sv = 0.0f;
-            int32_t pv = 0;
+            float sv;
+            int32_t pv;
+        };
+        // Chunk c covers source rows [c0, c0 + C) and is stored one row lower.
+        // The body is branch-free so that the compiler can keep the next
+        // chunk's loads in flight across the wait for this chunk: sources past
+        // the last row read the last row again, and destinations past it land
+        // on row budget - 1, which the incoming row overwrites at the end.
+        const int last = budget - 1;
+        auto load = [&](Chunk &ch, int c0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int src = c0 + u * kRowsPerPass + sub;
-                if (src < budget) d[u] = ld16<KVX_DECODE_NT>(base + (size_t)src * R::kBytes + part * 16);
+                const int src = min(c0 + u * kRowsPerPass + sub, last);
+                ch.d[u] = ld16<KVX_DECODE_NT>(base + (size_t)src * R::kBytes);
             }
-            if (t < C && c0 + t < budget) {
-                sv = sc[c0 + t];
-                pv = pc[c0 + t];
+            const int sr = min(c0 + (t % C), last);
+            ch.sv = sc[sr];
+            ch.pv = pc[sr];
+        };
+        // Make the compiler wait for this chunk's loads (and only those).
+        auto landed = [&](Chunk &ch) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) asm volatile("" ::"v"(ch.d[u].x), "v"(ch.d[u].y), "v"(ch.d[u].z), "v"(ch.d[u].w));
+            asm volatile("" ::"v"(ch.sv), "v"(ch.pv));
+        };
+        auto store = [&](const Chunk &ch, int c0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int dst = min(c0 + u * kRowsPerPass + sub - 1, last);
+                st16<KVX_DECODE_NT>(base + (size_t)dst * R::kBytes, ch.d[u]);
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (t < C) {
+                const int dr = min(c0 + t - 1, last);
+                sc[dr] = ch.sv;
+                pc[dr] = ch.pv;
+            }
+        };
+        // Software pipeline: the next chunk's loads are in flight while this
+        // chunk waits, meets the barrier and is stored.  The next chunk's
+        // sources lie above every row this chunk writes (except the clamped
+        // last row, whose value is discarded), and every thread has its loads
+        // of this chunk back before the barrier, so no row is overwritten
+        // before it has been read.
+        Chunk a, b;
+        int c0 = victim + 1;
+        load(a, c0);
+        while (true) {
+            const int c1 = c0 + C;
+            load(b, c1);
+            landed(a);
             __syncthreads();
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int src = c0 + u * kRowsPerPass + sub;
-                if (src < budget) st16<KVX_DECODE_NT>(base + (size_t)(src - 1) * R::kBytes + part * 16, d[u]);
-            }
-            if (t < C && c0 + t < budget) {
-                sc[c0 + t - 1] = sv;
-                pc[c0 + t - 1] = pv;
-            }
+            store(a, c0);
+            if (c1 >= budget) break;
+            const int c2 = c1 + C;
+            load(a, c2);
+            landed(b);
+            __syncthreads();
+            store(b, c1);
+            if (c2 >= budget) break;
+            c0 = c2;
         }
+        // Every store (including the discarded ones on row budget - 1) must be
+        // complete before the incoming row is written there.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
         dst_new = budget - 1;
     }
     if (t < kSlots) {
@@ -549,22 +656,31 @@ int validate_select_sizes(const kvx_shape &shape, int64_t n_kept, int64_t S, con
     return KVX_OK;
 }
 
+template <int DT, int MODE>
+int launch_score_mode(const void *k_new, int64_t G, const kvx_shape &sh, int64_t S, const float *filters,
+                      float sign, float *s_new, hipStream_t st) {
+    constexpr int U = KVX_SCORE_U;
+    constexpr int kRowsPerBlock = (KVX_SCORE_BLOCK / 64) * (64 / Row<DT>::kLanes) * U;
+    const uint32_t BH = (uint32_t)(sh.B * sh.H), H = (uint32_t)sh.H;
+    if (S >= kRowsPerBlock / 2) {
+        const uint32_t tiles = (uint32_t)((S + kRowsPerBlock - 1) / kRowsPerBlock);
+        if ((int64_t)tiles * G > INT32_MAX) return set_error(KVX_ERANGE, "qf_score_keys: grid too large");
+        score_tile_kernel<DT, MODE, U><<<(uint32_t)(tiles * G), KVX_SCORE_BLOCK, 0, st>>>(
+            (const char *)k_new, (uint32_t)S, tiles, BH, H, filters, sign, s_new);
+    } else {
+        const uint32_t n_rows = (uint32_t)(G * S);
+        const uint32_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+        score_flat_kernel<DT, MODE, U><<<blocks, KVX_SCORE_BLOCK, 0, st>>>(
+            (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, sign, s_new);
+    }
+    return check_launch("qf_score_keys");
+}
+
 template <int DT>
 int launch_score(const void *k_new, int64_t G, const kvx_shape &sh, int64_t S, int32_t mode,
                  const float *filters, int32_t sign, float *s_new, hipStream_t st) {
-    constexpr int U = KVX_SCORE_U;
-    constexpr int kRowsPerBlock = (KVX_SCORE_BLOCK / 64) * (64 / Row<DT>::kLanes) * U;
-    const uint32_t n_rows = (uint32_t)(G * S);
-    uint32_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    if (KVX_SCORE_BLOCKS_PER_CU > 0 && blocks > 256u * KVX_SCORE_BLOCKS_PER_CU) blocks = 256u * KVX_SCORE_BLOCKS_PER_CU;
-    const uint32_t BH = (uint32_t)(sh.B * sh.H), H = (uint32_t)sh.H;
-    if (mode == KVX_SCORE_L2)
-        score_kernel<DT, KVX_SCORE_L2, U><<<blocks, KVX_SCORE_BLOCK, 0, st>>>(
-            (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, 1.0f, s_new);
-    else
-        score_kernel<DT, KVX_SCORE_PROJ, U><<<blocks, KVX_SCORE_BLOCK, 0, st>>>(
-            (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, (float)sign, s_new);
-    return check_launch("qf_score_keys");
+    if (mode == KVX_SCORE_L2) return launch_score_mode<DT, KVX_SCORE_L2>(k_new, G, sh, S, filters, 1.0f, s_new, st);
+    return launch_score_mode<DT, KVX_SCORE_PROJ>(k_new, G, sh, S, filters, (float)sign, s_new, st);
 }
 
 template <int DT>
@@ -644,6 +760,7 @@ KVX_API int kv_evict_topk(const float *s_kept, const float *s_new, kvx_shape sha
     const uint32_t grid = (uint32_t)G;
     constexpr int NT = KVX_SELECT_NT;
     static_assert(NT == 256 || NT == 512 || NT == 1024, "selection block size");
+    // keys per thread: the smallest power of two covering n_total (<= KVX_MAX_TOTAL)
     if (n_total <= NT)
         select_kernel<1, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
     else if (n_total <= 2 * NT)
@@ -654,10 +771,12 @@ KVX_API int kv_evict_topk(const float *s_kept, const float *s_new, kvx_shape sha
         select_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
     else if (n_total <= 16 * NT)
         select_kernel<16, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-    else if (n_total <= 32 * NT)
-        select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-    else
-        select_kernel<64, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    else if constexpr (KVX_MAX_TOTAL > 16 * NT) {
+        if (n_total <= 32 * NT)
+            select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        else
+            select_kernel<64, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    }
     return check_launch("kv_evict_topk");
 }
 
@@ -716,11 +835,11 @@ KVX_API int kv_evict_one_inplace(void *k_cache, void *v_cache, float *s_cache, i
     if (G > INT32_MAX) return set_error(KVX_ERANGE, "kv_evict_one_inplace: too many groups");
     const int kl = p.keep == KVX_KEEP_LOW;
     if (shape.dtype == KVX_BF16)
-        evict_one_kernel<KVX_BF16, 8><<<(uint32_t)G, 256, 0, st>>>(
+        evict_one_kernel<KVX_BF16, KVX_DECODE_U><<<(uint32_t)G, KVX_DECODE_BLOCK, 0, st>>>(
             (char *)k_cache, (char *)v_cache, s_cache, pos_cache, (const char *)k_new, (const char *)v_new, s_new,
             (int32_t)pos_base, (int)n_kept, (int)p.budget, (int)p.n_sink, (int)p.recent, kl);
     else
-        evict_one_kernel<KVX_F32, 8><<<(uint32_t)G, 256, 0, st>>>(
+        evict_one_kernel<KVX_F32, KVX_DECODE_U><<<(uint32_t)G, KVX_DECODE_BLOCK, 0, st>>>(
             (char *)k_cache, (char *)v_cache, s_cache, pos_cache, (const char *)k_new, (const char *)v_new, s_new,
             (int32_t)pos_base, (int)n_kept, (int)p.budget, (int)p.n_sink, (int)p.recent, kl);
     return check_launch("kv_evict_one_inplace");
