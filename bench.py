@@ -187,7 +187,7 @@ def algorithmic_bytes(torch, wl):
     return total, dom
 
 
-def timed_steps(torch, wl, n):
+def timed_steps(torch, wl, n, graph=None):
     """Mean milliseconds per step over n steps.  Without snapshots the steps run
     back to back between two events; with snapshots every step is bracketed by
     its own events and the untimed restore runs between them."""
@@ -201,7 +201,10 @@ def timed_steps(torch, wl, n):
             s.wait_event(start)
         with torch.cuda.stream(s0):
             for _ in range(k):
-                wl.step()
+                if graph is not None:
+                    graph.replay()
+                else:
+                    wl.step()
         for s in rest:
             j = ev()
             j.record(s)
@@ -302,6 +305,8 @@ def main():
                     help="run the step's independent scorer runs on this many streams")
     ap.add_argument("--cpu-groups", type=int, default=32, help="groups in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as one captured HIP graph (workloads without snapshots, one stream)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for byte counters)")
     args = ap.parse_args()
@@ -330,9 +335,21 @@ def main():
 
     step_bytes, dom_bytes = algorithmic_bytes(torch, wl)
     log("algorithmic bytes per step: %.3f GB" % (step_bytes / 1e9))
+    graph = None
+    if args.graph:
+        if wl.snapshots or len(streams) > 1:
+            log("--graph needs a workload without snapshots on one stream")
+            sys.exit(2)
+        with torch.cuda.stream(streams[0]):
+            wl.step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=streams[0]):
+            wl.step()
+        torch.cuda.synchronize()
     if args.warmup:
-        timed_steps(torch, wl, args.warmup)
-    ms_per_step = timed_steps(torch, wl, args.steps)
+        timed_steps(torch, wl, args.warmup, graph)
+    ms_per_step = timed_steps(torch, wl, args.steps, graph)
 
     per = kernel_times(torch, wl, args.steps)
     breakdown = {n: {"launches_per_step": len(v) // args.steps, "mean_us": round(1e3 * sum(v) / len(v), 2)}
@@ -365,7 +382,7 @@ def main():
             "aniso": "drift*mu + N(0,0.25)", "lognorm": "r*u, ln r ~ N(0,0.25)", "gauss": "N(0,1)"}[cfg.keys],
         "config": {"workload": DESCRIPTIONS[args.workload], "groups": cfg.G,
                    "tokens_per_step": wl.tokens_per_step, "runs_per_step": len(wl.plans),
-                   "budget": cfg.budget, "streams": args.streams, "device": dev_name},
+                   "budget": cfg.budget, "streams": args.streams, "graph": bool(graph), "device": dev_name},
         "step_algorithmic_GBps": round(step_gbps, 1), "step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
         "step_algorithmic_bytes": int(step_bytes),
         "roofline": roof,

@@ -37,7 +37,8 @@
  *     positions [G, budget] int32; rows [0, n_kept) are valid, in temporal
  *     order.  Incoming buffers have S rows per group: K/V [G, S, D],
  *     scores [G, S].  All row-major and contiguous.
- *   - Element types: KVX_BF16 (raw bfloat16) or KVX_F32 for K/V rows; D = 128.
+ *   - Element types: KVX_BF16 (raw bfloat16), KVX_F16 or KVX_F32 for K/V rows;
+ *     head dim D of 64, 128 or 256 (rows are D elements).
  */
 #ifndef KVEVICT_H
 #define KVEVICT_H
@@ -62,6 +63,7 @@ extern "C" {
 /* Element types of K/V rows. */
 #define KVX_F32 0
 #define KVX_BF16 1
+#define KVX_F16 2  /* IEEE binary16 (the Metal kernels' key type, Q-Filters page, "Metal kernels") */
 
 /* Scorers. */
 #define KVX_SCORE_L2 0   /* s = ||k||_2                       */
@@ -72,14 +74,14 @@ extern "C" {
 #define KVX_KEEP_LOW 1   /* keep the lowest scores (L2 norm, paper rule)      */
 
 /* Bounds of this implementation. */
-#define KVX_HEAD_DIM 128     /* the only supported D                          */
+#define KVX_HEAD_DIM 128     /* the head dim of every workload here; D may also be 64 or 256 */
 #define KVX_MAX_BUDGET 8192  /* largest budget kv_evict_topk accepts          */
 #define KVX_MAX_TOTAL 16384  /* largest n_kept + S that one selection handles */
 
 typedef struct {
     int64_t L, B, H; /* layers, batch, KV heads: G = L*B*H groups            */
-    int64_t D;       /* head dim; must be KVX_HEAD_DIM                       */
-    int32_t dtype;   /* KVX_BF16 or KVX_F32                                  */
+    int64_t D;       /* head dim: 64, 128 or 256                             */
+    int32_t dtype;   /* KVX_BF16, KVX_F16 or KVX_F32                         */
 } kvx_shape;
 
 typedef struct {
@@ -109,7 +111,7 @@ KVX_API int kvx_abi_version(void);
 
 /*
  * qf_score_keys -- step 1: one score per incoming row.
- *   k_new    device [G, S, D] K rows (shape.dtype)
+ *   k_new    device [G, S, D] K rows (shape.dtype), widened exactly to float32
  *   S        incoming rows per group (S == 0: nothing is launched)
  *   mode     KVX_SCORE_L2: s = ||k||_2   (L2Norm page, "How it works" step 1)
  *            KVX_SCORE_PROJ: s = sign * sum_d k_d f[l][h][d]

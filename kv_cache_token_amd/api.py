@@ -14,7 +14,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import (KVX_BF16, KVX_F32, KVX_HEAD_DIM, KVX_KEEP_HIGH, KVX_KEEP_LOW, KVX_SCORE_L2,
+from ._lib import (KVX_BF16, KVX_F16, KVX_F32, KVX_HEAD_DIM, KVX_KEEP_HIGH, KVX_KEEP_LOW, KVX_SCORE_L2,
                    KVX_SCORE_PROJ, KvxParams, KvxShape, KvxStats, call)
 
 D = KVX_HEAD_DIM
@@ -29,18 +29,20 @@ def dtype_code(dtype) -> int:
     torch = _torch()
     if dtype in ("bf16", torch.bfloat16, KVX_BF16):
         return KVX_BF16
+    if dtype in ("f16", torch.float16, KVX_F16):
+        return KVX_F16
     if dtype in ("f32", torch.float32, KVX_F32):
         return KVX_F32
-    raise ValueError("unsupported K/V dtype %r (bf16 or f32)" % (dtype,))
+    raise ValueError("unsupported K/V dtype %r (bf16, f16 or f32)" % (dtype,))
 
 
 def torch_dtype(code: int):
     torch = _torch()
-    return torch.bfloat16 if code == KVX_BF16 else torch.float32
+    return {KVX_BF16: torch.bfloat16, KVX_F16: torch.float16, KVX_F32: torch.float32}[code]
 
 
-def make_shape(L: int, B: int, H: int, dtype) -> KvxShape:
-    return KvxShape(L, B, H, D, dtype_code(dtype))
+def make_shape(L: int, B: int, H: int, dtype, D_: int = D) -> KvxShape:
+    return KvxShape(L, B, H, D_, dtype_code(dtype))
 
 
 def make_params(budget: int, n_sink: int, recent: int, keep) -> KvxParams:
@@ -106,8 +108,8 @@ def qf_score_keys(k_new, shape: KvxShape, S: int, mode, filters, sign: int, s_ne
     """Score G*S incoming rows into s_new [G, S] (float32)."""
     torch = _torch()
     G, m = _G(shape), mode_code(mode)
-    kp = _dev(k_new, "k_new", torch_dtype(shape.dtype), G * S * D)
-    fp = _dev(filters, "filters", torch.float32, shape.L * shape.H * D, allow_none=(m == KVX_SCORE_L2))
+    kp = _dev(k_new, "k_new", torch_dtype(shape.dtype), G * S * shape.D)
+    fp = _dev(filters, "filters", torch.float32, shape.L * shape.H * shape.D, allow_none=(m == KVX_SCORE_L2))
     sp = _dev(s_new, "s_new", torch.float32, G * S)
     return _dispatch("qf_score_keys", (kp, shape, S, m, fp, sign, sp, _stream(stream)), prepare)
 
@@ -134,21 +136,21 @@ def kv_compact_gather(k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, pos
                       shape: KvxShape, n_kept: int, S: int, params: KvxParams, k_out, v_out, s_out, pos_out,
                       stream=None, prepare: bool = False):
     torch = _torch()
-    G, td, cap = _G(shape), torch_dtype(shape.dtype), params.budget
+    G, td, cap, Dd = _G(shape), torch_dtype(shape.dtype), params.budget, shape.D
     evict = n_kept + S > cap
     args = [
-        _dev(k_kept, "k_kept", td, G * cap * D, allow_none=(n_kept == 0)),
-        _dev(v_kept, "v_kept", td, G * cap * D, allow_none=(n_kept == 0)),
+        _dev(k_kept, "k_kept", td, G * cap * Dd, allow_none=(n_kept == 0)),
+        _dev(v_kept, "v_kept", td, G * cap * Dd, allow_none=(n_kept == 0)),
         _dev(s_kept, "s_kept", torch.float32, G * cap, allow_none=(n_kept == 0)),
         _dev(pos_kept, "pos_kept", torch.int32, G * cap, allow_none=(n_kept == 0)),
-        _dev(k_new, "k_new", td, G * S * D, allow_none=(S == 0)),
-        _dev(v_new, "v_new", td, G * S * D, allow_none=(S == 0)),
+        _dev(k_new, "k_new", td, G * S * Dd, allow_none=(S == 0)),
+        _dev(v_new, "v_new", td, G * S * Dd, allow_none=(S == 0)),
         _dev(s_new, "s_new", torch.float32, G * S, allow_none=(S == 0)),
         pos_base,
         _dev(keep_idx, "keep_idx", torch.int32, G * cap, allow_none=not evict),
         shape, n_kept, S, params,
-        _dev(k_out, "k_out", td, G * cap * D),
-        _dev(v_out, "v_out", td, G * cap * D),
+        _dev(k_out, "k_out", td, G * cap * Dd),
+        _dev(v_out, "v_out", td, G * cap * Dd),
         _dev(s_out, "s_out", torch.float32, G * cap),
         _dev(pos_out, "pos_out", torch.int32, G * cap),
         _stream(stream),
@@ -159,10 +161,10 @@ def kv_compact_gather(k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, pos
 def kv_evict_one_inplace(k_cache, v_cache, s_cache, pos_cache, k_new, v_new, s_new, pos_base: int,
                          shape: KvxShape, n_kept: int, params: KvxParams, stream=None, prepare: bool = False):
     torch = _torch()
-    G, td, cap = _G(shape), torch_dtype(shape.dtype), params.budget
-    args = (_dev(k_cache, "k_cache", td, G * cap * D), _dev(v_cache, "v_cache", td, G * cap * D),
+    G, td, cap, Dd = _G(shape), torch_dtype(shape.dtype), params.budget, shape.D
+    args = (_dev(k_cache, "k_cache", td, G * cap * Dd), _dev(v_cache, "v_cache", td, G * cap * Dd),
             _dev(s_cache, "s_cache", torch.float32, G * cap), _dev(pos_cache, "pos_cache", torch.int32, G * cap),
-            _dev(k_new, "k_new", td, G * D), _dev(v_new, "v_new", td, G * D),
+            _dev(k_new, "k_new", td, G * Dd), _dev(v_new, "v_new", td, G * Dd),
             _dev(s_new, "s_new", torch.float32, G), pos_base, shape, n_kept, params, _stream(stream))
     return _dispatch("kv_evict_one_inplace", args, prepare)
 
@@ -194,13 +196,14 @@ def qf_filters_from_queries(q: np.ndarray, H_kv: int) -> np.ndarray:
     return out
 
 
-def qf_filters_from_keys(k: np.ndarray, n: int) -> np.ndarray:
-    """k: [G, rows, D] float32 or bf16 bits (uint16); uses each group's first n rows."""
+def qf_filters_from_keys(k: np.ndarray, n: int, dtype: str = "bf16") -> np.ndarray:
+    """k: [G, rows, D] float32, or uint16 bits of bf16 / f16 (per `dtype`); uses
+    each group's first n rows."""
     k = np.ascontiguousarray(k)
     G, rows, Dd = k.shape
-    dt = KVX_F32 if k.dtype == np.float32 else KVX_BF16
     if k.dtype not in (np.float32, np.uint16):
-        raise TypeError("keys must be float32 or bf16 bits (uint16)")
+        raise TypeError("keys must be float32 or 16-bit bits (uint16)")
+    dt = KVX_F32 if k.dtype == np.float32 else (KVX_F16 if dtype == "f16" else KVX_BF16)
     out = np.empty((G, Dd), dtype=np.float32)
     call("qf_filters_from_keys", k.ctypes.data, dt, G, n, rows, Dd, out.ctypes.data)
     return out

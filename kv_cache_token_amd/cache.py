@@ -21,13 +21,15 @@ D = api.D
 class EvictingCache:
     def __init__(self, L: int, B: int, H: int, budget: int, n_sink: int = 4, recent: int = 0,
                  keep: str = "low", mode: str = "l2", filters=None, sign: int = 1, dtype: str = "bf16",
-                 device="cuda", calib_tokens: int = 0, stream=None):
+                 device="cuda", calib_tokens: int = 0, stream=None, head_dim: int = 128):
         import torch
         self.L, self.B, self.H, self.G = L, B, H, L * B * H
         self.budget, self.n_sink, self.recent = budget, n_sink, recent
         self.mode, self.sign = mode, sign
         self.keep = "high" if mode == "proj" else keep
-        self.shape = api.make_shape(L, B, H, dtype)
+        self.D = head_dim
+        self.dtype_name = {"bf16": "bf16", "f16": "f16", "f32": "f32"}.get(dtype, dtype)
+        self.shape = api.make_shape(L, B, H, dtype, head_dim)
         self.params = api.make_params(budget, n_sink, recent, self.keep)
         self.calib_tokens = calib_tokens
         self.stream = stream
@@ -44,8 +46,8 @@ class EvictingCache:
         G = self.G
 
         def bufset():
-            return (torch.empty((G, budget, D), dtype=td, device=self.device),
-                    torch.empty((G, budget, D), dtype=td, device=self.device),
+            return (torch.empty((G, budget, head_dim), dtype=td, device=self.device),
+                    torch.empty((G, budget, head_dim), dtype=td, device=self.device),
                     torch.empty((G, budget), dtype=torch.float32, device=self.device),
                     torch.empty((G, budget), dtype=torch.int32, device=self.device))
 
@@ -68,10 +70,10 @@ class EvictingCache:
         f = torch.as_tensor(np.asarray(filters, dtype=np.float32) if not isinstance(filters, torch.Tensor)
                             else filters, dtype=torch.float32)
         if per_group:
-            f = f.reshape(self.L * self.B, self.H, D)
-            self.score_shape = api.make_shape(self.L * self.B, 1, self.H, self.shape.dtype)
+            f = f.reshape(self.L * self.B, self.H, self.D)
+            self.score_shape = api.make_shape(self.L * self.B, 1, self.H, self.shape.dtype, self.D)
         else:
-            f = f.reshape(self.L, self.H, D)
+            f = f.reshape(self.L, self.H, self.D)
             self.score_shape = self.shape
         self.filters = f.to(self.device).contiguous()
 
@@ -82,11 +84,12 @@ class EvictingCache:
                                       "rows (the pre-calibration passthrough is not implemented)")
         import torch
         first = k_new[:, :self.calib_tokens].contiguous().cpu()
-        if first.dtype == torch.bfloat16:
+        if first.dtype in (torch.bfloat16, torch.float16):
             host = first.view(torch.int16).numpy().view(np.uint16)
         else:
             host = first.numpy()
-        self.set_filters(api.qf_filters_from_keys(host, self.calib_tokens), per_group=True)
+        dt = "f16" if first.dtype == torch.float16 else "bf16"
+        self.set_filters(api.qf_filters_from_keys(host, self.calib_tokens, dt), per_group=True)
 
     # -- state -------------------------------------------------------------
     @property
@@ -130,8 +133,8 @@ class EvictingCache:
 
     def _step(self, k_new, v_new, prepare: bool):
         S = k_new.shape[-2]
-        k_new = k_new.contiguous().reshape(self.G, S, D)
-        v_new = v_new.contiguous().reshape(self.G, S, D)
+        k_new = k_new.contiguous().reshape(self.G, S, self.D)
+        v_new = v_new.contiguous().reshape(self.G, S, self.D)
         calls = []
         if S == 0:
             return calls, (k_new, v_new)

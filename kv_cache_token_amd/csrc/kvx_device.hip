@@ -11,20 +11,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kvevict.h"
 #include "kvx_common.h"
 
 namespace kvx {
 namespace {
 
-constexpr int kD = KVX_HEAD_DIM;
-
-template <int DT>
+// A K/V row of HD elements of type DT, read 16 bytes per lane.
+template <int DT, int HD>
 struct Row {
-    static constexpr int kElemBytes = DT == KVX_BF16 ? 2 : 4;
-    static constexpr int kBytes = kD * kElemBytes;   // 256 (bf16) or 512 (fp32)
+    static constexpr int kElemBytes = DT == KVX_F32 ? 4 : 2;
+    static constexpr int kBytes = HD * kElemBytes;    // e.g. 256 B for a bf16 row of 128
     static constexpr int kLanes = kBytes / 16;        // lanes covering one row, 16 B each
     static constexpr int kElemsPerLane = 16 / kElemBytes;
+    static_assert(kLanes >= 1 && kLanes <= 64 && (kLanes & (kLanes - 1)) == 0,
+                  "a row spans a power-of-two number of lanes of one wave");
 };
 
 // Tuning knobs (compile-time): rows in flight per lane and cache hints.
@@ -84,10 +87,17 @@ __device__ __forceinline__ void st16(char *p, uint4 v) {
         *reinterpret_cast<u32x4 *>(p) = w;
 }
 
-// Widen the 16 bytes a lane holds to float32 (exact for both element types).
+// Widen the 16 bytes a lane holds to float32 (exact for every element type).
 template <int DT>
 __device__ __forceinline__ void widen(uint4 r, float *x) {
-    if constexpr (DT == KVX_BF16) {
+    if constexpr (DT == KVX_F16) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] & 0xFFFFu));
+            x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] >> 16));
+        }
+    } else if constexpr (DT == KVX_BF16) {
         const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -119,9 +129,9 @@ __device__ __forceinline__ uint32_t select_key(float s, int keep_low) {
 // on the tile it falls in or on the grid.  A lane always covers the same slice
 // of the head dim, so its slice of the group's filter stays in registers.
 // ---------------------------------------------------------------------------
-template <int DT, int MODE>
+template <int DT, int HD, int MODE>
 __device__ __forceinline__ float row_partial(uint4 raw, const float *f) {
-    using R = Row<DT>;
+    using R = Row<DT, HD>;
     float x[R::kElemsPerLane];
     widen<DT>(raw, x);
     float acc = 0.0f;
@@ -133,11 +143,11 @@ __device__ __forceinline__ float row_partial(uint4 raw, const float *f) {
     return acc;
 }
 
-template <int DT>
+template <int DT, int HD>
 __device__ __forceinline__ void load_filter_slice(const float *__restrict__ filt, uint32_t l, uint32_t h,
                                                   uint32_t H, uint32_t part, float *f) {
-    using R = Row<DT>;
-    const float4 *f4 = reinterpret_cast<const float4 *>(filt + (size_t)(l * H + h) * kD + part * R::kElemsPerLane);
+    using R = Row<DT, HD>;
+    const float4 *f4 = reinterpret_cast<const float4 *>(filt + (size_t)(l * H + h) * HD + part * R::kElemsPerLane);
 #pragma unroll
     for (int q = 0; q < R::kElemsPerLane / 4; ++q) {
         const float4 v = f4[q];
@@ -155,11 +165,11 @@ __device__ __forceinline__ float finish_score(int mode, float acc, float sign) {
 
 // Group-major tiles: block b scores rows [tile*RPB, tile*RPB + RPB) of group
 // b / tiles (used when a group has at least a tile of rows).
-template <int DT, int MODE, int U>
+template <int DT, int HD, int MODE, int U>
 __global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_tile_kernel(
     const char *__restrict__ k, uint32_t S, uint32_t tiles, uint32_t BH, uint32_t H,
     const float *__restrict__ filt, float sign, float *__restrict__ out) {
-    using R = Row<DT>;
+    using R = Row<DT, HD>;
     constexpr int kRowsPerLoad = 64 / R::kLanes;
     constexpr int kRowsPerWave = kRowsPerLoad * U;
     const uint32_t g = blockIdx.x / tiles;
@@ -169,7 +179,7 @@ __global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_tile_kernel(
     const uint32_t r0 = tile * (KVX_SCORE_BLOCK / 64) * kRowsPerWave + (threadIdx.x >> 6) * kRowsPerWave;
     const char *kg = k + (size_t)g * S * R::kBytes;
     float f[R::kElemsPerLane];
-    if constexpr (MODE == KVX_SCORE_PROJ) load_filter_slice<DT>(filt, g / BH, g % H, H, part, f);
+    if constexpr (MODE == KVX_SCORE_PROJ) load_filter_slice<DT, HD>(filt, g / BH, g % H, H, part, f);
     uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -179,18 +189,18 @@ __global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_tile_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t r = r0 + u * kRowsPerLoad + sub;
-        const float acc = row_partial<DT, MODE>(raw[u], f);
+        const float acc = row_partial<DT, HD, MODE>(raw[u], f);
         if (part == 0 && r < S) out[(size_t)g * S + r] = finish_score(MODE, acc, sign);
     }
 }
 
 // Flat rows (a group has fewer rows than a tile, e.g. one decode token): row r
 // belongs to group r / S.
-template <int DT, int MODE, int U>
+template <int DT, int HD, int MODE, int U>
 __global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_flat_kernel(
     const char *__restrict__ k, uint32_t n_rows, uint32_t S, uint32_t BH, uint32_t H,
     const float *__restrict__ filt, float sign, float *__restrict__ out) {
-    using R = Row<DT>;
+    using R = Row<DT, HD>;
     constexpr int kRowsPerLoad = 64 / R::kLanes;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t sub = lane / R::kLanes, part = lane % R::kLanes;
@@ -208,9 +218,9 @@ __global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_flat_kernel(
         float f[R::kElemsPerLane];
         if constexpr (MODE == KVX_SCORE_PROJ) {
             const uint32_t g = r < n_rows ? r / S : 0u;
-            load_filter_slice<DT>(filt, g / BH, g % H, H, part, f);
+            load_filter_slice<DT, HD>(filt, g / BH, g % H, H, part, f);
         }
-        const float acc = row_partial<DT, MODE>(raw[u], f);
+        const float acc = row_partial<DT, HD, MODE>(raw[u], f);
         if (part == 0 && r < n_rows) out[r] = finish_score(MODE, acc, sign);
     }
 }
@@ -410,7 +420,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
 // V; the lane with part == 0 also moves the score and the position.
 // keep_idx == nullptr means the identity (nothing evicted).
 // ---------------------------------------------------------------------------
-template <int DT, int U>
+template <int DT, int HD, int U>
 __global__ __launch_bounds__(KVX_GATHER_BLOCK) void gather_kernel(
     const char *__restrict__ k_kept, const char *__restrict__ v_kept,
     const float *__restrict__ s_kept, const int32_t *__restrict__ pos_kept,
@@ -418,7 +428,7 @@ __global__ __launch_bounds__(KVX_GATHER_BLOCK) void gather_kernel(
     const float *__restrict__ s_new, int32_t pos_base, const int32_t *__restrict__ keep_idx,
     int n_kept, int S, int budget, int j0, int n_out, int blocks_per_group, char *__restrict__ k_out,
     char *__restrict__ v_out, float *__restrict__ s_out, int32_t *__restrict__ pos_out) {
-    using R = Row<DT>;
+    using R = Row<DT, HD>;
     constexpr int kRowsPerPass = KVX_GATHER_BLOCK / R::kLanes;
     const int g = blockIdx.x / blocks_per_group;
     const int b = blockIdx.x - g * blocks_per_group;
@@ -471,13 +481,13 @@ __global__ __launch_bounds__(KVX_GATHER_BLOCK) void gather_kernel(
 // then the chunk is stored one row lower.  A chunk only writes rows below the
 // next chunk's sources, so chunk-by-chunk order makes the shift race-free.
 // ---------------------------------------------------------------------------
-template <int DT, int U>
+template <int DT, int HD, int U>
 __global__ __launch_bounds__(KVX_DECODE_BLOCK) void evict_one_kernel(
     char *__restrict__ k_cache, char *__restrict__ v_cache, float *__restrict__ s_cache,
     int32_t *__restrict__ pos_cache, const char *__restrict__ k_new, const char *__restrict__ v_new,
     const float *__restrict__ s_new, int32_t pos_base, int n_kept, int budget, int n_sink,
     int recent, int keep_low) {
-    using R = Row<DT>;
+    using R = Row<DT, HD>;
     constexpr int kSlots = 2 * R::kLanes;          // K lanes then V lanes of one row
     constexpr int NB = KVX_DECODE_BLOCK;
     constexpr int kRowsPerPass = NB / kSlots;
@@ -610,9 +620,10 @@ int check_shape(const kvx_shape &sh, int64_t *G) {
     if (sh.L < 0 || sh.B < 0 || sh.H < 0)
         return set_error(KVX_EINVAL, "shape: L, B, H must be >= 0 (got %lld, %lld, %lld)",
                          (long long)sh.L, (long long)sh.B, (long long)sh.H);
-    if (sh.D != kD) return set_error(KVX_EINVAL, "shape: D must be %d (got %lld)", kD, (long long)sh.D);
-    if (sh.dtype != KVX_BF16 && sh.dtype != KVX_F32)
-        return set_error(KVX_EINVAL, "shape: dtype must be KVX_BF16 or KVX_F32 (got %d)", (int)sh.dtype);
+    if (sh.D != 64 && sh.D != 128 && sh.D != 256)
+        return set_error(KVX_EINVAL, "shape: D must be 64, 128 or 256 (got %lld)", (long long)sh.D);
+    if (sh.dtype != KVX_BF16 && sh.dtype != KVX_F32 && sh.dtype != KVX_F16)
+        return set_error(KVX_EINVAL, "shape: dtype must be KVX_BF16, KVX_F16 or KVX_F32 (got %d)", (int)sh.dtype);
     if (sh.L > INT32_MAX || sh.B > INT32_MAX || sh.H > INT32_MAX ||
         (sh.L > 0 && sh.B > 0 && sh.H > 0 && sh.L * sh.B > INT32_MAX / sh.H))
         return set_error(KVX_ERANGE, "shape: L*B*H must be below 2^31");
@@ -641,6 +652,26 @@ int check_launch(const char *what) {
     return KVX_OK;
 }
 
+// Calls f(DT, HD) with compile-time constants for the shape's element type and
+// head dim.  `copy_only` maps fp16 onto bf16 (same row bytes) for kernels that
+// only move rows.
+template <class F>
+int dispatch_row(const kvx_shape &sh, bool copy_only, F &&f) {
+    using bf = std::integral_constant<int, KVX_BF16>;
+    using hf = std::integral_constant<int, KVX_F16>;
+    using fp = std::integral_constant<int, KVX_F32>;
+    auto by_d = [&](auto dt) -> int {
+        switch (sh.D) {
+            case 64: return f(dt, std::integral_constant<int, 64>{});
+            case 128: return f(dt, std::integral_constant<int, 128>{});
+            default: return f(dt, std::integral_constant<int, 256>{});
+        }
+    };
+    if (sh.dtype == KVX_F32) return by_d(fp{});
+    if (sh.dtype == KVX_F16 && !copy_only) return by_d(hf{});
+    return by_d(bf{});
+}
+
 int validate_select_sizes(const kvx_shape &shape, int64_t n_kept, int64_t S, const kvx_evict_params &p,
                           int64_t *G) {
     int rc = check_shape(shape, G);
@@ -656,46 +687,47 @@ int validate_select_sizes(const kvx_shape &shape, int64_t n_kept, int64_t S, con
     return KVX_OK;
 }
 
-template <int DT, int MODE>
+template <int DT, int HD, int MODE>
 int launch_score_mode(const void *k_new, int64_t G, const kvx_shape &sh, int64_t S, const float *filters,
                       float sign, float *s_new, hipStream_t st) {
     constexpr int U = KVX_SCORE_U;
-    constexpr int kRowsPerBlock = (KVX_SCORE_BLOCK / 64) * (64 / Row<DT>::kLanes) * U;
+    constexpr int kRowsPerBlock = (KVX_SCORE_BLOCK / 64) * (64 / Row<DT, HD>::kLanes) * U;
     const uint32_t BH = (uint32_t)(sh.B * sh.H), H = (uint32_t)sh.H;
     if (S >= kRowsPerBlock / 2) {
         const uint32_t tiles = (uint32_t)((S + kRowsPerBlock - 1) / kRowsPerBlock);
         if ((int64_t)tiles * G > INT32_MAX) return set_error(KVX_ERANGE, "qf_score_keys: grid too large");
-        score_tile_kernel<DT, MODE, U><<<(uint32_t)(tiles * G), KVX_SCORE_BLOCK, 0, st>>>(
+        score_tile_kernel<DT, HD, MODE, U><<<(uint32_t)(tiles * G), KVX_SCORE_BLOCK, 0, st>>>(
             (const char *)k_new, (uint32_t)S, tiles, BH, H, filters, sign, s_new);
     } else {
         const uint32_t n_rows = (uint32_t)(G * S);
         const uint32_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-        score_flat_kernel<DT, MODE, U><<<blocks, KVX_SCORE_BLOCK, 0, st>>>(
+        score_flat_kernel<DT, HD, MODE, U><<<blocks, KVX_SCORE_BLOCK, 0, st>>>(
             (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, sign, s_new);
     }
     return check_launch("qf_score_keys");
 }
 
-template <int DT>
+template <int DT, int HD>
 int launch_score(const void *k_new, int64_t G, const kvx_shape &sh, int64_t S, int32_t mode,
                  const float *filters, int32_t sign, float *s_new, hipStream_t st) {
-    if (mode == KVX_SCORE_L2) return launch_score_mode<DT, KVX_SCORE_L2>(k_new, G, sh, S, filters, 1.0f, s_new, st);
-    return launch_score_mode<DT, KVX_SCORE_PROJ>(k_new, G, sh, S, filters, (float)sign, s_new, st);
+    if (mode == KVX_SCORE_L2)
+        return launch_score_mode<DT, HD, KVX_SCORE_L2>(k_new, G, sh, S, filters, 1.0f, s_new, st);
+    return launch_score_mode<DT, HD, KVX_SCORE_PROJ>(k_new, G, sh, S, filters, (float)sign, s_new, st);
 }
 
-template <int DT>
+template <int DT, int HD>
 int launch_gather(const void *k_kept, const void *v_kept, const float *s_kept, const int32_t *pos_kept,
                   const void *k_new, const void *v_new, const float *s_new, int32_t pos_base,
                   const int32_t *keep_idx, int64_t G, int n_kept, int S, int budget, int j0, int n_out,
                   void *k_out, void *v_out, float *s_out, int32_t *pos_out, hipStream_t st) {
     constexpr int U = KVX_GATHER_U;
-    constexpr int kRowsPerBlock = (KVX_GATHER_BLOCK / Row<DT>::kLanes) * U;
+    constexpr int kRowsPerBlock = (KVX_GATHER_BLOCK / Row<DT, HD>::kLanes) * U;
     const int rows = n_out - j0;
     if (rows <= 0 || G == 0) return KVX_OK;
     const int bpg = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     const int64_t blocks = G * bpg;
     if (blocks > INT32_MAX) return set_error(KVX_ERANGE, "kv_compact_gather: grid too large");
-    gather_kernel<DT, U><<<(uint32_t)blocks, KVX_GATHER_BLOCK, 0, st>>>(
+    gather_kernel<DT, HD, U><<<(uint32_t)blocks, KVX_GATHER_BLOCK, 0, st>>>(
         (const char *)k_kept, (const char *)v_kept, s_kept, pos_kept, (const char *)k_new,
         (const char *)v_new, s_new, pos_base, keep_idx, n_kept, S, budget, j0, n_out, bpg,
         (char *)k_out, (char *)v_out, s_out, pos_out);
@@ -726,8 +758,10 @@ KVX_API int qf_score_keys(const void *k_new, kvx_shape shape, int64_t S, int32_t
     if (G * S >= ((int64_t)1 << 31)) return set_error(KVX_ERANGE, "qf_score_keys: G*S must be below 2^31");
     if (!k_new || !s_new) return set_error(KVX_EINVAL, "qf_score_keys: NULL buffer");
     hipStream_t st = (hipStream_t)stream;
-    return shape.dtype == KVX_BF16 ? launch_score<KVX_BF16>(k_new, G, shape, S, mode, filters, sign, s_new, st)
-                                   : launch_score<KVX_F32>(k_new, G, shape, S, mode, filters, sign, s_new, st);
+    return dispatch_row(shape, false, [&](auto dt, auto hd) {
+        return launch_score<decltype(dt)::value, decltype(hd)::value>(k_new, G, shape, S, mode, filters, sign,
+                                                                       s_new, st);
+    });
 }
 
 KVX_API int kv_evict_workspace_size(kvx_shape shape, int64_t n_kept, int64_t S, kvx_evict_params p,
@@ -810,13 +844,11 @@ KVX_API int kv_compact_gather(const void *k_kept, const void *v_kept, const floa
     const int j0 = n_alias == 4 ? (int)n_kept : 0;  // in place: only the incoming rows move
     const int32_t *idx = evict ? keep_idx : nullptr;
     hipStream_t st = (hipStream_t)stream;
-    if (shape.dtype == KVX_BF16)
-        return launch_gather<KVX_BF16>(k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, (int32_t)pos_base,
-                                       idx, G, (int)n_kept, (int)S, (int)p.budget, j0, n_out, k_out, v_out,
-                                       s_out, pos_out, st);
-    return launch_gather<KVX_F32>(k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, (int32_t)pos_base, idx,
-                                  G, (int)n_kept, (int)S, (int)p.budget, j0, n_out, k_out, v_out, s_out,
-                                  pos_out, st);
+    return dispatch_row(shape, true, [&](auto dt, auto hd) {
+        return launch_gather<decltype(dt)::value, decltype(hd)::value>(
+            k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, (int32_t)pos_base, idx, G, (int)n_kept, (int)S,
+            (int)p.budget, j0, n_out, k_out, v_out, s_out, pos_out, st);
+    });
 }
 
 KVX_API int kv_evict_one_inplace(void *k_cache, void *v_cache, float *s_cache, int32_t *pos_cache,
@@ -834,14 +866,14 @@ KVX_API int kv_evict_one_inplace(void *k_cache, void *v_cache, float *s_cache, i
     hipStream_t st = (hipStream_t)stream;
     if (G > INT32_MAX) return set_error(KVX_ERANGE, "kv_evict_one_inplace: too many groups");
     const int kl = p.keep == KVX_KEEP_LOW;
-    if (shape.dtype == KVX_BF16)
-        evict_one_kernel<KVX_BF16, KVX_DECODE_U><<<(uint32_t)G, KVX_DECODE_BLOCK, 0, st>>>(
-            (char *)k_cache, (char *)v_cache, s_cache, pos_cache, (const char *)k_new, (const char *)v_new, s_new,
-            (int32_t)pos_base, (int)n_kept, (int)p.budget, (int)p.n_sink, (int)p.recent, kl);
-    else
-        evict_one_kernel<KVX_F32, KVX_DECODE_U><<<(uint32_t)G, KVX_DECODE_BLOCK, 0, st>>>(
-            (char *)k_cache, (char *)v_cache, s_cache, pos_cache, (const char *)k_new, (const char *)v_new, s_new,
-            (int32_t)pos_base, (int)n_kept, (int)p.budget, (int)p.n_sink, (int)p.recent, kl);
+    dispatch_row(shape, true, [&](auto dt, auto hd) {
+        evict_one_kernel<decltype(dt)::value, decltype(hd)::value, KVX_DECODE_U>
+            <<<(uint32_t)G, KVX_DECODE_BLOCK, 0, st>>>((char *)k_cache, (char *)v_cache, s_cache, pos_cache,
+                                                       (const char *)k_new, (const char *)v_new, s_new,
+                                                       (int32_t)pos_base, (int)n_kept, (int)p.budget,
+                                                       (int)p.n_sink, (int)p.recent, kl);
+        return 0;
+    });
     return check_launch("kv_evict_one_inplace");
 }
 

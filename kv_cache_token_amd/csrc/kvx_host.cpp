@@ -127,6 +127,30 @@ int top_right_singular(const std::vector<double> &X, int64_t m, int n, std::vect
     return KVX_OK;
 }
 
+// IEEE binary16 bits to double (exact; subnormals, infinities and NaN kept).
+double half_to_double(uint16_t h) {
+    const int sign = h >> 15, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = std::ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = std::ldexp((double)(m | 0x400), e - 25);
+    return sign ? -v : v;
+}
+
+// Element i of a K/V row buffer of the given type, widened to double.
+double widen_elem(const void *k, int32_t dtype, int64_t i) {
+    if (dtype == KVX_F32) return ((const float *)k)[i];
+    const uint16_t b = ((const uint16_t *)k)[i];
+    if (dtype == KVX_F16) return half_to_double(b);
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
 // Runs fn(i) for i in [0, n) on up to 16 worker threads.
 template <class F>
 void parallel_for(int64_t n, F fn) {
@@ -527,7 +551,8 @@ KVX_API int qf_filters_from_keys(const void *k, int32_t dtype, int64_t G, int64_
     clear_error();
     if (!k || !out || G < 0 || n <= 1 || D <= 0 || D > 4096 || group_stride < n)
         return set_error(KVX_EINVAL, "qf_filters_from_keys: bad arguments");
-    if (dtype != KVX_BF16 && dtype != KVX_F32) return set_error(KVX_EINVAL, "qf_filters_from_keys: bad dtype");
+    if (dtype != KVX_BF16 && dtype != KVX_F32 && dtype != KVX_F16)
+        return set_error(KVX_EINVAL, "qf_filters_from_keys: bad dtype");
     const int dd = (int)D;
     std::vector<int> status((size_t)G, KVX_OK);
     std::vector<const char *> why((size_t)G, "");
@@ -535,16 +560,7 @@ KVX_API int qf_filters_from_keys(const void *k, int32_t dtype, int64_t G, int64_
         std::vector<double> X((size_t)(n * D));
         for (int64_t r = 0; r < n; ++r)
             for (int i = 0; i < dd; ++i) {
-                const int64_t e = (g * group_stride + r) * D + i;
-                double x;
-                if (dtype == KVX_BF16) {
-                    const uint32_t u = (uint32_t)((const uint16_t *)k)[e] << 16;
-                    float fv;
-                    memcpy(&fv, &u, 4);
-                    x = fv;
-                } else {
-                    x = ((const float *)k)[e];
-                }
+                const double x = widen_elem(k, dtype, (g * group_stride + r) * D + i);
                 if (!std::isfinite(x)) {
                     status[g] = KVX_EINVAL;
                     why[g] = "non-finite key";
@@ -575,9 +591,9 @@ KVX_API int qf_filters_from_keys(const void *k, int32_t dtype, int64_t G, int64_
 KVX_API int kvx_stats(kvx_shape shape, int64_t tokens_seen, int64_t tokens_kept, int32_t mode, kvx_stats_t *out) {
     clear_error();
     if (!out || shape.L < 0 || shape.B < 0 || shape.H < 0 || shape.D <= 0 || tokens_seen < 0 || tokens_kept < 0 ||
-        tokens_kept > tokens_seen || (shape.dtype != KVX_BF16 && shape.dtype != KVX_F32))
+        tokens_kept > tokens_seen || (shape.dtype != KVX_BF16 && shape.dtype != KVX_F32 && shape.dtype != KVX_F16))
         return set_error(KVX_EINVAL, "kvx_stats: bad arguments");
-    const int64_t G = shape.L * shape.B * shape.H, es = shape.dtype == KVX_BF16 ? 2 : 4;
+    const int64_t G = shape.L * shape.B * shape.H, es = shape.dtype == KVX_F32 ? 4 : 2;
     out->tokens_seen = tokens_seen;
     out->tokens_kept = tokens_kept;
     out->kept_bytes = G * tokens_kept * 2 * shape.D * es;

@@ -124,6 +124,20 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def f16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16 (nearest, ties to even); raw uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def bits_to_f32(b: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float32 values of stored rows (float32, bf16 bits or f16 bits)."""
+    if dtype == "f32":
+        return np.asarray(b, dtype=np.float32)
+    if dtype == "f16":
+        return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+    return bf16_bits_to_f32(b)
+
+
 def planted_mu(cfg: Config, l: int, h: int) -> np.ndarray:
     """Unit direction mu_{l,h} (float64) planted in the anisotropic key recipe."""
     m = _rng(cfg.cid, l, 0, h, 0, TAG_MU).standard_normal(D)
@@ -161,8 +175,17 @@ def _values_f32(cfg: Config, g: int, chunk: int, S: int) -> np.ndarray:
     return _rng(cfg.cid, l, b, h, chunk, TAG_V).standard_normal((S, D), dtype=np.float32)
 
 
+def encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values -> stored row bytes of `dtype` (float32, bf16 or f16 bits)."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return f16_bits_from_f32(x)
+    return bf16_bits_from_f32(x)
+
+
 def _encode(cfg: Config, x: np.ndarray) -> np.ndarray:
-    return x if cfg.dtype == "f32" else bf16_bits_from_f32(x)
+    return encode(x, cfg.dtype)
 
 
 def group_chunk(cfg: Config, g: int, chunk: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -214,7 +237,7 @@ def custom_keys(shape: Tuple[int, ...], seed: int, dtype: str = "bf16", scale: f
         x = base[pick]
     else:
         raise ValueError(kind)
-    return x if dtype == "f32" else bf16_bits_from_f32(x)
+    return encode(x, dtype)
 
 
 # ----------------------------------------------------------------------------
@@ -269,7 +292,8 @@ def host_to_torch(x: np.ndarray, dtype: str):
     import torch
     if dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    t16 = torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint16).view(np.int16))
+    return t16.view(torch.float16 if dtype == "f16" else torch.bfloat16)
 
 
 def torch_to_host(t, dtype: str) -> np.ndarray:

@@ -32,7 +32,8 @@ _LIB = os.path.join(_HERE, "libkvx_oracle.so")
 _lib = None
 
 MODE_L2, MODE_PROJ = 0, 1
-DT_F32, DT_BF16 = 0, 1
+DT_F32, DT_BF16, DT_F16 = 0, 1, 2
+_DT = {"f32": DT_F32, "bf16": DT_BF16, "f16": DT_F16}
 
 
 def build(force: bool = True) -> str:
@@ -76,25 +77,28 @@ def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _dt(x: np.ndarray) -> int:
+def _dt(x: np.ndarray, dtype: Optional[str] = None) -> int:
+    """Element type code of a key array: float32, or raw 16-bit bits (uint16)
+    read as bf16 unless dtype says "f16"."""
     if x.dtype == np.float32:
         return DT_F32
     if x.dtype == np.uint16:
-        return DT_BF16
-    raise TypeError("keys must be float32 or bf16 bits (uint16), got %s" % x.dtype)
+        return DT_F16 if dtype == "f16" else DT_BF16
+    raise TypeError("keys must be float32 or 16-bit bits (uint16), got %s" % x.dtype)
 
 
 def num_threads() -> int:
     return lib().orc_num_threads()
 
 
-def score(k: np.ndarray, mode: str = "l2", f: Optional[np.ndarray] = None, sign: int = 1) -> np.ndarray:
-    """Scores [n] float32 of rows k [n, D] (float32 or bf16 bits)."""
+def score(k: np.ndarray, mode: str = "l2", f: Optional[np.ndarray] = None, sign: int = 1,
+          dtype: Optional[str] = None) -> np.ndarray:
+    """Scores [n] float32 of rows k [n, D] (float32, or bf16 / f16 bits)."""
     k = np.ascontiguousarray(k)
     n, D = k.shape
     out = np.empty(n, dtype=np.float32)
     ff = None if f is None else np.ascontiguousarray(f, dtype=np.float32)
-    _check(lib().orc_score(_ptr(k), _dt(k), n, D, MODE_L2 if mode == "l2" else MODE_PROJ,
+    _check(lib().orc_score(_ptr(k), _dt(k, dtype), n, D, MODE_L2 if mode == "l2" else MODE_PROJ,
                            _ptr(ff), sign, _ptr(out)), "orc_score")
     return out
 
@@ -112,7 +116,7 @@ def select(s: np.ndarray, budget: int, n_sink: int, recent: int, keep: str) -> n
 class OracleCache:
     """State of G independent groups (the kept rows of each), absorbing blocks.
 
-    Arrays: ``k``/``v`` [G, budget, D] (float32 or uint16 bf16 bits), ``s`` [G, budget]
+    Arrays: ``k``/``v`` [G, budget, D] (float32, or uint16 bits of bf16 / f16), ``s`` [G, budget]
     float32 stored scores, ``pos`` [G, budget] int32, ``n`` [G] kept counts,
     ``tokens`` [G] tokens seen (the true offset)."""
 
@@ -141,7 +145,7 @@ class OracleCache:
             raise OracleError("projection mode needs filters")
         si = None if scores_in is None else np.ascontiguousarray(scores_in, dtype=np.float32).reshape(G, S)
         _check(lib().orc_groups_update(
-            G, self.budget, D, DT_F32 if self.dtype == "f32" else DT_BF16,
+            G, self.budget, D, _DT[self.dtype],
             MODE_L2 if self.mode == "l2" else MODE_PROJ, _ptr(self.filters), self.sign,
             self.budget, self.n_sink, self.recent, 1 if self.keep == "low" else 0,
             _ptr(self.k), _ptr(self.v), _ptr(self.s), _ptr(self.pos), _ptr(self.n),

@@ -43,7 +43,23 @@
 #define ORC_ENOMEM -2
 #define ORC_ENONFINITE -3
 
-/* dtype: 0 = float32 rows, 1 = bfloat16 rows (raw uint16 bits). */
+/*
+ * dtype: 0 = float32 rows, 1 = bfloat16 rows, 2 = IEEE binary16 rows (raw
+ * uint16 bits for both 16-bit types).  Widening is exact.
+ */
+static double half_bits_to_double(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                /* zero or subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m | 0x400), e - 25);   /* (1.m) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
 static double widen(const void *rows, int dtype, int64_t i)
 {
     if (dtype == 1) {
@@ -52,16 +68,18 @@ static double widen(const void *rows, int dtype, int64_t i)
         memcpy(&f, &u, sizeof f);
         return (double)f;
     }
+    if (dtype == 2)
+        return half_bits_to_double(((const uint16_t *)rows)[i]);
     return (double)((const float *)rows)[i];
 }
 
-static int64_t esize(int dtype) { return dtype == 1 ? 2 : 4; }
+static int64_t esize(int dtype) { return dtype == 0 ? 4 : 2; }
 
 /* Score n rows of D elements.  mode 0 = L2 norm, 1 = projection onto f with sign. */
 int orc_score(const void *k, int dtype, int64_t n, int64_t D, int mode,
               const float *f, int sign, float *out)
 {
-    if ((dtype != 0 && dtype != 1) || (mode != 0 && mode != 1) || D <= 0 || n < 0)
+    if ((dtype < 0 || dtype > 2) || (mode != 0 && mode != 1) || D <= 0 || n < 0)
         return ORC_EINVAL;
     if (mode == 1 && (f == NULL || (sign != 1 && sign != -1)))
         return ORC_EINVAL;

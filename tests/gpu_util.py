@@ -29,7 +29,7 @@ def say(msg: str) -> None:
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
-    return (synth.bf16_bits_to_f32(x) if dtype == "bf16" else x).astype(np.float64)
+    return synth.bits_to_f32(x, dtype).astype(np.float64)
 
 
 def score_scale(K: np.ndarray, dtype: str, mode: str, f=None) -> np.ndarray:
@@ -65,8 +65,8 @@ def gpu_state(cache, groups):
     k, v, s, p = cache.kept()
     out = {}
     for g in groups:
-        out[g] = (synth.torch_to_host(k[g], "bf16" if cache.shape.dtype == 1 else "f32"),
-                  synth.torch_to_host(v[g], "bf16" if cache.shape.dtype == 1 else "f32"),
+        out[g] = (synth.torch_to_host(k[g], cache.dtype_name),
+                  synth.torch_to_host(v[g], cache.dtype_name),
                   s[g].cpu().numpy(), p[g].cpu().numpy())
     return out
 

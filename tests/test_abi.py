@@ -51,8 +51,10 @@ def test_validation_rejects_bad_calls_without_launching():
         ("kv_evict_topk", (FAKE, FAKE, sh, 0, 10, api.make_params(64, 0, 0, 7), FAKE, None, 0, None), -1),
         ("kv_evict_topk", (FAKE, FAKE, sh, 0, 10, api.make_params(8193, 4, 0, "low"), FAKE, None, 0, None), -2),
         ("kv_evict_topk", (FAKE, FAKE, sh, 8192, 8193, api.make_params(8192, 4, 0, "low"), FAKE, None, 0, None), -2),
-        ("kv_evict_topk", (FAKE, FAKE, api.KvxShape(2, 1, 4, 64, 1), 0, 10, ok, FAKE, None, 0, None), -1),
+        ("kv_evict_topk", (FAKE, FAKE, api.KvxShape(2, 1, 4, 32, 1), 0, 10, ok, FAKE, None, 0, None), -1),
+        ("kv_evict_topk", (FAKE, FAKE, api.KvxShape(2, 1, 4, 512, 1), 0, 10, ok, FAKE, None, 0, None), -1),
         ("kv_evict_topk", (FAKE, FAKE, api.KvxShape(2, 1, 4, 128, 5), 0, 10, ok, FAKE, None, 0, None), -1),
+        ("kv_evict_topk", (FAKE, FAKE, api.KvxShape(2, 1, 4, 128, 3), 0, 10, ok, FAKE, None, 0, None), -1),
         ("kv_evict_topk", (FAKE, FAKE, sh, 0, -1, ok, FAKE, None, 0, None), -1),
         ("qf_score_keys", (FAKE, sh, 10, 1, None, 1, FAKE, None), -1),
         ("qf_score_keys", (FAKE, sh, 10, 1, FAKE, 2, FAKE, None), -1),
@@ -164,11 +166,22 @@ def test_key_filters_match_oracle_on_fallback_workload():
         api.qf_filters_from_keys(np.ones((1, 10, D), np.float32), 10)
 
 
+def test_key_filters_read_f16_and_fp32_rows_like_bf16():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((2, 200, D)) * 0.5 + rng.standard_normal(D) * 0.2).astype(np.float32)
+    for dt in ("f16", "bf16"):
+        bits = synth.encode(x, dt)
+        got = api.qf_filters_from_keys(bits, 128, dt)
+        exact = api.qf_filters_from_keys(synth.bits_to_f32(bits, dt), 128)
+        assert np.array_equal(got, exact)
+
+
 def test_byte_accounting():
     st = api.kvx_stats(api.make_shape(28, 1, 8, "bf16"), 4096, 512, "proj")
     row = 2 * D * 2
     assert st["kept_bytes"] == 224 * 512 * row and st["full_seq_bytes"] == 224 * 4096 * row
     assert st["compression_ratio"] == 8.0 and st["filter_bytes"] == 28 * 8 * D * 4
     assert api.kvx_stats(api.make_shape(1, 1, 1, "f32"), 10, 10, "l2")["filter_bytes"] == 0
+    assert api.kvx_stats(api.make_shape(1, 1, 1, "f16", 64), 10, 5, "l2")["kept_bytes"] == 5 * 2 * 64 * 2
     with pytest.raises(KvxError):
         api.kvx_stats(api.make_shape(1, 1, 1, "f32"), 10, 11, "l2")

@@ -41,10 +41,10 @@ def _api():
 def _score_gpu(K, dtype, mode, f_lh, sign, L, B, H):
     import torch
     api = _api()
-    G, S = K.shape[0], K.shape[1]
+    G, S, Dd = K.shape
     out = torch.full((G, S), float("nan"), dtype=torch.float32, device="cuda")
     fd = None if f_lh is None else torch.from_numpy(np.ascontiguousarray(f_lh, np.float32)).cuda()
-    api.qf_score_keys(_t(K, dtype), api.make_shape(L, B, H, dtype), S, mode, fd, sign, out)
+    api.qf_score_keys(_t(K, dtype), api.make_shape(L, B, H, dtype, Dd), S, mode, fd, sign, out)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -55,35 +55,38 @@ def _group_filters(f_lh, L, B, H):
 
 # --------------------------------------------------------------------------- score
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Dd", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("mode,sign", [("l2", 1), ("proj", 1), ("proj", -1)])
-def test_score_bit_exact_on_exact_inputs(dtype, mode, sign):
+def test_score_bit_exact_on_exact_inputs(dtype, mode, sign, Dd):
     L, B, H, S = 2, 3, 4, 333
     G = L * B * H
-    say("score exact %s %s %d" % (dtype, mode, sign))
-    K = np.stack([synth.custom_keys((S, D), 300 + g, dtype, kind="int") for g in range(G)])
+    say("score exact %s %s %d D=%d" % (dtype, mode, sign, Dd))
+    K = np.stack([synth.custom_keys((S, Dd), 300 + g, dtype, kind="int") for g in range(G)])
     rng = np.random.default_rng(1)
-    f_lh = (rng.integers(-64, 65, size=(L, H, D)) / 64.0).astype(np.float32) if mode == "proj" else None
+    f_lh = (rng.integers(-64, 65, size=(L, H, Dd)) / 64.0).astype(np.float32) if mode == "proj" else None
     got = _score_gpu(K, dtype, mode, f_lh, sign, L, B, H)
     fg = _group_filters(f_lh, L, B, H) if mode == "proj" else [None] * G
-    want = np.stack([oracle.score(K[g], mode, fg[g], sign) for g in range(G)])
+    want = np.stack([oracle.score(K[g], mode, fg[g], sign, dtype) for g in range(G)])
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Dd", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("mode,sign", [("l2", 1), ("proj", 1), ("proj", -1)])
-def test_score_within_tolerance(dtype, mode, sign):
+def test_score_within_tolerance(dtype, mode, sign, Dd):
     L, B, H, S = 3, 2, 8, 1001
     G = L * B * H
-    say("score tol %s %s %d" % (dtype, mode, sign))
-    K = np.stack([synth.custom_keys((S, D), 400 + g, dtype, scale=10.0 ** (g % 5 - 2)) for g in range(G)])
+    say("score tol %s %s %d D=%d" % (dtype, mode, sign, Dd))
+    scale_of = (lambda g: 10.0 ** (g % 3 - 1)) if dtype == "f16" else (lambda g: 10.0 ** (g % 5 - 2))
+    K = np.stack([synth.custom_keys((S, Dd), 400 + g, dtype, scale=scale_of(g)) for g in range(G)])
     rng = np.random.default_rng(2)
-    f_lh = rng.standard_normal((L, H, D)).astype(np.float32) if mode == "proj" else None
+    f_lh = rng.standard_normal((L, H, Dd)).astype(np.float32) if mode == "proj" else None
     if f_lh is not None:
         f_lh /= np.linalg.norm(f_lh, axis=2, keepdims=True)
     got = _score_gpu(K, dtype, mode, f_lh, sign, L, B, H)
     fg = _group_filters(f_lh, L, B, H) if mode == "proj" else [None] * G
-    want = np.stack([oracle.score(K[g], mode, fg[g], sign) for g in range(G)])
+    want = np.stack([oracle.score(K[g], mode, fg[g], sign, dtype) for g in range(G)])
     scale = np.stack([score_scale(K[g], dtype, mode, fg[g]) for g in range(G)])
     assert_scores_close(got, want, scale, "score")
     if mode == "proj" and sign == -1:
@@ -191,20 +194,23 @@ def test_select_real_infinities_rank_below_protected_rows():
 
 # --------------------------------------------------------------------------- gather
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("n_kept,S,budget", [(0, 300, 128), (128, 200, 128), (100, 28, 128), (128, 1, 128),
-                                             (4096, 4096, 4096), (37, 91, 64)])
-def test_gather_bit_exact(dtype, n_kept, S, budget):
+GATHER_SIZES = [(0, 300, 128), (128, 200, 128), (100, 28, 128), (128, 1, 128), (4096, 4096, 4096), (37, 91, 64)]
+GATHER_CASES = [("bf16", 128) + c for c in GATHER_SIZES] + [("f32", 128) + c for c in GATHER_SIZES] + \
+    [(dt, Dd, 37, 91, 64) for dt in ("bf16", "f16", "f32") for Dd in (64, 256)] + [("f16", 128, 128, 200, 128)]
+
+
+@pytest.mark.parametrize("dtype,Dd,n_kept,S,budget", GATHER_CASES, ids=[str(c) for c in GATHER_CASES])
+def test_gather_bit_exact(dtype, Dd, n_kept, S, budget):
     import torch
     api = _api()
-    say("gather %s %d %d %d" % (dtype, n_kept, S, budget))
+    say("gather %s D=%d %d %d %d" % (dtype, Dd, n_kept, S, budget))
     G, n_sink, recent = 5, 2, 3
-    shape, params = api.make_shape(1, 1, G, dtype), api.make_params(budget, n_sink, recent, "low")
+    shape, params = api.make_shape(1, 1, G, dtype, Dd), api.make_params(budget, n_sink, recent, "low")
     rng = np.random.default_rng(n_kept + S)
-    Kc = synth.custom_keys((G, budget, D), 700, dtype)
-    Vc = synth.custom_keys((G, budget, D), 701, dtype)
-    Kn = synth.custom_keys((G, S, D), 702, dtype)
-    Vn = synth.custom_keys((G, S, D), 703, dtype)
+    Kc = synth.custom_keys((G, budget, Dd), 700, dtype)
+    Vc = synth.custom_keys((G, budget, Dd), 701, dtype)
+    Kn = synth.custom_keys((G, S, Dd), 702, dtype)
+    Vn = synth.custom_keys((G, S, Dd), 703, dtype)
     sc = rng.standard_normal((G, budget)).astype(np.float32)
     pc = np.sort(rng.choice(10 ** 6, size=(G, budget), replace=False), axis=1).astype(np.int32)
     sn = rng.standard_normal((G, S)).astype(np.float32)
@@ -242,18 +248,22 @@ def test_gather_bit_exact(dtype, n_kept, S, budget):
 
 # --------------------------------------------------------------------------- decode
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("recent,keep", [(0, "low"), (1, "high"), (8, "low"), (8, "high")])
-def test_decode_inplace_lockstep_with_oracle(dtype, recent, keep):
+DECODE_CASES = [(dt, 128, r, k) for dt in ("bf16", "f32") for r, k in ((0, "low"), (1, "high"), (8, "low"), (8, "high"))] \
+    + [("f16", 128, 8, "low"), ("bf16", 64, 8, "high"), ("bf16", 256, 8, "low"), ("f32", 256, 0, "low"),
+       ("f16", 64, 1, "low")]
+
+
+@pytest.mark.parametrize("dtype,Dd,recent,keep", DECODE_CASES, ids=[str(c) for c in DECODE_CASES])
+def test_decode_inplace_lockstep_with_oracle(dtype, Dd, recent, keep):
     import torch
     from kv_cache_token_amd.cache import EvictingCache
-    say("decode %s %d %s" % (dtype, recent, keep))
+    say("decode %s D=%d %d %s" % (dtype, Dd, recent, keep))
     G, T, budget, n_sink = 4, 300, 64, 2
-    K = np.stack([synth.custom_keys((T, D), 800 + g, dtype, kind="dup") for g in range(G)])
-    V = np.stack([synth.custom_keys((T, D), 900 + g, dtype) for g in range(G)])
+    K = np.stack([synth.custom_keys((T, Dd), 800 + g, dtype, kind="dup") for g in range(G)])
+    V = np.stack([synth.custom_keys((T, Dd), 900 + g, dtype) for g in range(G)])
     dK, dV = _t(K, dtype), _t(V, dtype)
-    c = EvictingCache(1, 1, G, budget, n_sink, recent, keep, "l2", dtype=dtype)
-    o = oracle.OracleCache(G, D, dtype, budget, n_sink, recent, keep)
+    c = EvictingCache(1, 1, G, budget, n_sink, recent, keep, "l2", dtype=dtype, head_dim=Dd)
+    o = oracle.OracleCache(G, Dd, dtype, budget, n_sink, recent, keep)
     for t in range(T):
         c.update(dK[:, t:t + 1].contiguous(), dV[:, t:t + 1].contiguous())
         s_gpu = c.last_scores().cpu().numpy()

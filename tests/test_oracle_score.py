@@ -101,3 +101,31 @@ def test_bf16_rounding_helper_matches_numpy_definition():
     x = (rng.standard_normal(200000) * rng.lognormal(0, 3, 200000)).astype(np.float32)
     x[:6] = [0.0, -0.0, 1.0, 1.00390625, 1.005859375, -3.0e-39]   # ties and a subnormal
     assert np.array_equal(synth.bf16_bits_from_f32(x), synth.bf16_bits_from_f32_np(x))
+
+
+def test_f16_widening_definition_and_numpy_route():
+    bits = np.zeros((1, D), dtype=np.uint16)
+    bits[0, :4] = [0x3C00, 0xC000, 0x4200, 0x0000]   # 1, -2, 3, 0 -> norm sqrt(14)
+    assert oracle.score(bits, "l2", dtype="f16")[0] == np.float32(math.sqrt(14.0))
+    # the largest normal, the smallest subnormal and a mid subnormal, against numpy's float16
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((500, D)) * rng.lognormal(0, 4, (500, 1))).astype(np.float16)
+    x[0, :3] = [65504.0, 2.0 ** -24, 3 * 2.0 ** -20]
+    x[~np.isfinite(x)] = 1.0
+    got = oracle.score(x.view(np.uint16), "l2", dtype="f16")
+    want = np.linalg.norm(x.astype(np.float64), axis=1).astype(np.float32)
+    ulp = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1 and (ulp == 0).mean() > 0.99
+
+
+@pytest.mark.parametrize("Dd", [64, 256])
+def test_other_head_dims_match_numpy(Dd):
+    rng = np.random.default_rng(Dd)
+    k = rng.standard_normal((300, Dd)).astype(np.float32)
+    f = rng.standard_normal(Dd).astype(np.float32)
+    got = oracle.score(k, "proj", f, 1)
+    want = (k.astype(np.float64) @ f.astype(np.float64)).astype(np.float32)
+    ulp = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1 and (ulp == 0).mean() > 0.99
+    kb = synth.encode(k, "bf16")
+    assert np.array_equal(oracle.score(kb, "l2"), oracle.score(synth.bits_to_f32(kb, "bf16"), "l2"))
