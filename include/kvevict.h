@@ -75,8 +75,9 @@ extern "C" {
 
 /* Bounds of this implementation. */
 #define KVX_HEAD_DIM 128     /* the head dim of every workload here; D may also be 64 or 256 */
-#define KVX_MAX_BUDGET 8192  /* largest budget kv_evict_topk accepts          */
-#define KVX_MAX_TOTAL 16384  /* largest n_kept + S that one selection handles */
+#define KVX_MAX_BUDGET (1 << 21)   /* largest budget accepted                          */
+#define KVX_MAX_TOTAL (1 << 22)    /* largest n_kept + S that one selection handles     */
+#define KVX_ONCHIP_TOTAL 32768     /* up to this n_total the selection needs no workspace */
 
 typedef struct {
     int64_t L, B, H; /* layers, batch, KV heads: G = L*B*H groups            */
@@ -130,10 +131,14 @@ KVX_API int qf_score_keys(const void *k_new, kvx_shape shape, int64_t S, int32_t
                           const float *filters, int32_t sign, float *s_new, void *stream);
 
 /*
- * kv_evict_workspace_size -- device workspace kv_evict_topk needs for these
- * sizes.  The current selection runs in on-chip memory and needs none
- * (*bytes = 0); the call exists so that callers stay correct if a later
- * selection needs scratch.  Errors: as kv_evict_topk's validation.
+ * kv_evict_workspace_size -- bytes of device workspace kv_evict_topk needs for
+ * these sizes: 0 when n_kept + S <= KVX_ONCHIP_TOTAL (one workgroup per group
+ * selects on chip) or when nothing is evicted; otherwise
+ * G * (260 + 2 * ceil(n_total / 16384)) * 4 bytes for the multi-block
+ * selection's histograms, state and block counts.  The caller allocates it;
+ * kv_evict_topk initialises it itself on the stream (no memset needed), and
+ * calls that overlap on one workspace race.  Errors: as kv_evict_topk's
+ * validation.
  */
 KVX_API int kv_evict_workspace_size(kvx_shape shape, int64_t n_kept, int64_t S,
                                     kvx_evict_params p, size_t *bytes);
@@ -147,7 +152,8 @@ KVX_API int kv_evict_workspace_size(kvx_shape shape, int64_t n_kept, int64_t S,
  *            concatenation (row r < n_kept is kept row r, row r >= n_kept is
  *            incoming row r - n_kept), strictly ascending, min(n_total, budget)
  *            of them per group.
- *   ws       workspace of kv_evict_workspace_size bytes (may be NULL if 0)
+ *   ws       device workspace of at least kv_evict_workspace_size bytes
+ *            (may be NULL when that is 0); KVX_EINVAL if missing or too small
  * When n_total <= budget nothing is evicted and keep_idx is 0..n_total-1.
  * Otherwise the protected rows (r < n_sink, r >= n_total - recent) are kept,
  * and the other budget - n_sink - recent slots go to the best rows: highest

@@ -121,6 +121,17 @@ class EvictingCache:
         return api.kvx_stats(self.shape, self.tokens_seen, self.n_kept, self.mode)
 
     # -- the step ----------------------------------------------------------
+    def _workspace(self, n_kept: int, S: int):
+        """Device workspace the selection needs for this call (None when it
+        selects on chip); grown on demand and reused."""
+        import torch
+        need = api.kv_evict_workspace_size(self.shape, n_kept, S, self.params)
+        if need == 0:
+            return None
+        if getattr(self, "_ws", None) is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
     def _scores(self, S: int):
         import torch
         if self._s_new.shape[1] != S:
@@ -154,8 +165,8 @@ class EvictingCache:
             calls.append(api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, None, self.shape, nk, S,
                                                self.params, k, v, s, p, self.stream, prepare=prepare))
         else:
-            calls.append(api.kv_evict_topk(s, s_new, self.shape, nk, S, self.params, self.keep_idx, None,
-                                           self.stream, prepare=prepare))
+            calls.append(api.kv_evict_topk(s, s_new, self.shape, nk, S, self.params, self.keep_idx,
+                                           self._workspace(nk, S), self.stream, prepare=prepare))
             ko, vo, so, po = self._bufs[1 - self._cur]
             calls.append(api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, self.keep_idx,
                                                self.shape, nk, S, self.params, ko, vo, so, po, self.stream,

@@ -241,17 +241,160 @@ __device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// Steps 2-3: selection.  One workgroup of NT threads per group.  Thread t holds
-// the keys of rows t, t + NT, ... (M of them) in registers, so every load is
-// coalesced.  The budget-th largest key tau is found with four 8-bit radix
-// passes; each wave counts into its own LDS histogram (scores cluster, so a
-// shared histogram would serialise the waves on a few bins), the histograms of
-// the next pass are cleared while the current one is scanned, and one wave
-// sums the per-wave counts and scans them.  The kept rows are those with
-// key > tau plus the first `quota` rows (in row order) with key == tau; their
-// indices are written in row order using per-64-row chunk counts.  Protected
-// rows get key 0xFFFFFFFF, above every real score's key.
+// Steps 2-3: selection.
+//
+// Every row of the concatenation gets an order-preserving u32 key: protected
+// rows (the first n_sink, the last `recent`) get 0xFFFFFFFF, above every real
+// score's key.  tau = the budget-th largest key is found by four 8-bit radix
+// passes; the kept rows are those with key > tau plus the first `quota` rows
+// (in row order) with key == tau, and their indices are written in row order
+// from per-64-row chunk counts.
+//
+// Up to KVX_ONCHIP_TOTAL rows one workgroup per group does everything on chip.
+// Beyond that, a group's rows are split over blocks of MB_ROWS rows and the
+// passes meet in a small device workspace (histogram, state, block counts).
 // ---------------------------------------------------------------------------
+struct SelRows {
+    const float *sk;  // stored scores of the group's kept rows
+    const float *sn;  // scores of the group's incoming rows
+    int n_kept, n_total, n_sink, recent, keep_low;
+};
+
+__device__ __forceinline__ uint32_t row_key(const SelRows &a, int r) {
+    const float s = r < a.n_kept ? a.sk[r] : a.sn[r - a.n_kept];
+    const bool prot = r < a.n_sink || r >= a.n_total - a.recent;
+    return prot ? 0xFFFFFFFFu : select_key(s, a.keep_low);
+}
+
+// Load the keys of rows r0 + i*NT + t, i < M (rows past n_total get key 0 and
+// are never counted).
+template <int M, int NT>
+__device__ __forceinline__ void load_keys(const SelRows &a, int r0, uint32_t *key) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int r = r0 + i * NT + (int)threadIdx.x;
+        key[i] = r < a.n_total ? row_key(a, r) : 0u;
+    }
+}
+
+// Count the digit (key >> shift) & 255 of every key that matches the prefix
+// into this wave's 256-bin LDS histogram h.  While one digit covers many lanes
+// the increments are aggregated per wave; once digits spread, one per lane.
+template <int M, int NT>
+__device__ __forceinline__ void count_digits(const uint32_t *key, int r0, int n_total, uint32_t prefix,
+                                             uint32_t pmask, int shift, uint32_t *h) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int r = r0 + i * NT + (int)threadIdx.x;
+        bool act = r < n_total && (key[i] & pmask) == prefix;
+        const uint32_t d = (key[i] >> shift) & 0xFFu;
+        for (int it = 0; it < 4; ++it) {
+            const uint64_t am = __ballot(act);
+            if (am == 0) break;
+            const int leader = __ffsll((unsigned long long)am) - 1;
+            const uint32_t ld = __builtin_amdgcn_readlane(d, leader);
+            const bool mine = act && d == ld;
+            const uint32_t cnt = (uint32_t)__popcll(__ballot(mine));
+            if (lane == leader) atomicAdd(&h[ld], cnt);
+            if (mine) act = false;
+            if (cnt < 8) break;
+        }
+        if (act) atomicAdd(&h[d], 1u);
+    }
+}
+
+// One wave: lane l holds the counts of bins 255-4l (c.w) down to 252-4l (c.x).
+// Finds the bin where the krem-th largest key falls; the owning lane returns
+// true and sets the digit and the remaining rank inside that bin.
+__device__ __forceinline__ bool pick_digit(uint4 c, uint32_t krem, uint32_t *digit, uint32_t *nk) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t c0 = c.w, c1 = c.z, c2 = c.y, c3 = c.x;
+    const uint32_t local = c0 + c1 + c2 + c3;
+    const uint32_t incl = wave_prefix_incl(local);  // keys in this lane's bins or higher ones
+    const uint32_t above = incl - local;
+    if (!(above < krem && krem <= incl)) return false;
+    uint32_t cum = above;
+    if (cum + c0 >= krem) {
+        *digit = 255 - 4 * lane;
+    } else if ((cum += c0) + c1 >= krem) {
+        *digit = 254 - 4 * lane;
+    } else if ((cum += c1) + c2 >= krem) {
+        *digit = 253 - 4 * lane;
+    } else {
+        cum += c2;
+        *digit = 252 - 4 * lane;
+    }
+    *nk = krem - cum;
+    return true;
+}
+
+// Write the kept rows among rows r0 + i*NT + t (i < M) in row order:
+// out[base_gt + #(key > tau before) + min(base_eq + #(key == tau before), quota)].
+// `chunk` holds M*NT/64 counters.  Ends with the block synchronised.
+template <int M, int NT>
+__device__ __forceinline__ void write_kept(const uint32_t *key, int r0, int n_total, uint32_t tau, uint32_t quota,
+                                           uint32_t base_gt, uint32_t base_eq, int32_t *out, int budget,
+                                           uint32_t *chunk) {
+    constexpr int NW = NT / 64, NCH = M * NW, CPL = (NCH + 63) / 64;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int c = i * NW + w;
+        const int r = r0 + c * 64 + lane;
+        const bool valid = r < n_total;
+        const uint64_t gm = __ballot(valid && key[i] > tau);
+        const uint64_t em = __ballot(valid && key[i] == tau);
+        if (lane == 0) chunk[c] = ((uint32_t)__popcll(gm) << 16) | (uint32_t)__popcll(em);
+    }
+    __syncthreads();
+    if (w == 0) {  // exclusive scan of the packed (gt << 16 | eq) chunk counts
+        uint32_t a[CPL], local = 0;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = CPL * lane + j;
+            a[j] = c < NCH ? chunk[c] : 0u;
+            local += a[j];
+        }
+        uint32_t run = wave_prefix_incl(local) - local;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = CPL * lane + j;
+            if (c < NCH) chunk[c] = run;
+            run += a[j];
+        }
+    }
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int c = i * NW + w;
+        const int r = r0 + c * 64 + lane;
+        const bool valid = r < n_total;
+        const uint64_t gm = __ballot(valid && key[i] > tau);
+        const uint64_t em = __ballot(valid && key[i] == tau);
+        if (valid) {
+            const uint32_t base = chunk[c];
+            const uint32_t gb = base_gt + (base >> 16) + (uint32_t)__popcll(gm & below);
+            const uint32_t eb = base_eq + (base & 0xFFFFu) + (uint32_t)__popcll(em & below);
+            // Exactly `budget` rows qualify, so every slot is below budget; the
+            // bound check only keeps a corrupt input from writing past the row.
+            uint32_t slot = 0xFFFFFFFFu;
+            if (key[i] > tau)
+                slot = gb + min(eb, quota);
+            else if (key[i] == tau && eb < quota)
+                slot = gb + eb;
+            if (slot < (uint32_t)budget) out[slot] = r;
+        }
+    }
+    __syncthreads();
+}
+
+// One workgroup of NT threads per group; thread t holds the keys of rows
+// t, t + NT, ... (M of them) in registers, so every load is coalesced.  Each
+// wave counts into its own LDS histogram (scores cluster, so a shared one would
+// serialise the waves on a few bins); the next pass's histograms are cleared
+// while the current one is scanned.
 template <int M, int NT>
 __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_kept,
                                                       const float *__restrict__ s_new, int n_kept,
@@ -259,33 +402,23 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
                                                       int keep_low, int32_t *__restrict__ keep_idx) {
     constexpr int NW = NT / 64;
     const int g = blockIdx.x;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int t = threadIdx.x, w = t >> 6;
     const int n_total = n_kept + S;
     int32_t *out = keep_idx + (size_t)g * budget;
     if (n_total <= budget) {
         for (int r = t; r < n_total; r += NT) out[r] = r;
         return;
     }
-    const float *sk = s_kept + (size_t)g * budget;
-    const float *sn = s_new + (size_t)g * S;
+    const SelRows rows{s_kept + (size_t)g * budget, s_new + (size_t)g * S, n_kept, n_total, n_sink, recent,
+                       keep_low};
 
     __shared__ uint4 hist4[2][NW][64];  // per-wave 256-bin histograms, two passes' worth
     __shared__ uint32_t sel[2];
-    __shared__ uint32_t chunk[KVX_MAX_TOTAL / 64];
+    __shared__ uint32_t chunk[M * NW];
     uint32_t(*hist)[NW][256] = reinterpret_cast<uint32_t(*)[NW][256]>(hist4);
 
     uint32_t key[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-        const int r = i * NT + t;
-        uint32_t kk = 0;
-        if (r < n_total) {
-            const float s = r < n_kept ? sk[r] : sn[r - n_kept];
-            const bool prot = r < n_sink || r >= n_total - recent;
-            kk = prot ? 0xFFFFFFFFu : select_key(s, keep_low);
-        }
-        key[i] = kk;
-    }
+    load_keys<M, NT>(rows, 0, key);
     for (int i = t; i < NW * 64; i += NT) (&hist4[0][0][0])[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
@@ -293,59 +426,20 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        uint32_t *h = hist[pass & 1][w];
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-            const int r = i * NT + t;
-            bool act = r < n_total && (key[i] & pmask) == prefix;
-            const uint32_t d = (key[i] >> shift) & 0xFFu;
-            // Wave-aggregated increments while the leading digit covers many
-            // lanes; once the digits spread, one atomic per lane.
-            for (int it = 0; it < 4; ++it) {
-                const uint64_t am = __ballot(act);
-                if (am == 0) break;
-                const int leader = __ffsll((unsigned long long)am) - 1;
-                const uint32_t ld = __builtin_amdgcn_readlane(d, leader);
-                const bool mine = act && d == ld;
-                const uint32_t cnt = (uint32_t)__popcll(__ballot(mine));
-                if (lane == leader) atomicAdd(&h[ld], cnt);
-                if (mine) act = false;
-                if (cnt < 8) break;
-            }
-            if (act) atomicAdd(&h[d], 1u);
-        }
+        count_digits<M, NT>(key, 0, n_total, prefix, pmask, shift, hist[pass & 1][w]);
         __syncthreads();
         if (w == 0) {
-            // lane l owns bins 255-4l (c0) down to 252-4l (c3): higher bins in lower lanes
             uint4 c = make_uint4(0, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < NW; ++v) {
-                const uint4 x = hist4[pass & 1][v][63 - lane];
+                const uint4 x = hist4[pass & 1][v][63 - (t & 63)];
                 c.x += x.x;
                 c.y += x.y;
                 c.z += x.z;
                 c.w += x.w;
             }
-            const uint32_t c0 = c.w, c1 = c.z, c2 = c.y, c3 = c.x;
-            const uint32_t local = c0 + c1 + c2 + c3;
-            const uint32_t incl = wave_prefix_incl(local);  // keys in this lane's bins or higher ones
-            const uint32_t above = incl - local;
-            if (above < krem && krem <= incl) {
-                uint32_t cum = above, d, nk;
-                if (cum + c0 >= krem) {
-                    d = 255 - 4 * lane;
-                    nk = krem - cum;
-                } else if ((cum += c0) + c1 >= krem) {
-                    d = 254 - 4 * lane;
-                    nk = krem - cum;
-                } else if ((cum += c1) + c2 >= krem) {
-                    d = 253 - 4 * lane;
-                    nk = krem - cum;
-                } else {
-                    cum += c2;
-                    d = 252 - 4 * lane;
-                    nk = krem - cum;
-                }
+            uint32_t d, nk;
+            if (pick_digit(c, krem, &d, &nk)) {
                 sel[0] = d;
                 sel[1] = nk;
             }
@@ -357,61 +451,131 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
         pmask |= 0xFFu << shift;
         krem = sel[1];
     }
-    const uint32_t tau = prefix, quota = krem;
+    write_kept<M, NT>(key, 0, n_total, prefix, krem, 0, 0, out, budget, chunk);
+}
 
-    // Per-chunk (64 consecutive rows) counts of key > tau and key == tau,
-    // packed as (gt << 16) | eq; both stay below 2^16.
-    const int nchunks = (n_total + 63) >> 6;
+// --- multi-block selection (n_total above the on-chip bound) --------------
+// Workspace per group g: hist[256] | state[4] = {prefix, pmask, krem, -} |
+// counts[W][2] = {#key > tau, #key == tau} of each of the W row blocks.
+constexpr int MB_NT = 1024, MB_M = 16, MB_ROWS = MB_NT * MB_M;
+
+__host__ __device__ __forceinline__ size_t mb_words(int W) { return 256 + 4 + 2 * (size_t)W; }
+
+__global__ __launch_bounds__(256) void mb_init_kernel(uint32_t *__restrict__ ws, int W, int budget) {
+    uint32_t *h = ws + (size_t)blockIdx.x * mb_words(W);
+    h[threadIdx.x] = 0;
+    if (threadIdx.x < 4) h[256 + threadIdx.x] = threadIdx.x == 2 ? (uint32_t)budget : 0u;
+}
+
+struct MbArgs {
+    const float *s_kept, *s_new;
+    int n_kept, S, budget, n_sink, recent, keep_low, W;
+    uint32_t *ws;
+};
+
+__device__ __forceinline__ SelRows mb_rows(const MbArgs &a, int g) {
+    return SelRows{a.s_kept + (size_t)g * a.budget, a.s_new + (size_t)g * a.S, a.n_kept, a.n_kept + a.S,
+                   a.n_sink, a.recent, a.keep_low};
+}
+
+// Histogram of one radix pass over one row block, added into the group's
+// workspace histogram.
+__global__ __launch_bounds__(MB_NT) void mb_hist_kernel(MbArgs a, int shift) {
+    constexpr int NW = MB_NT / 64;
+    const int g = blockIdx.x / a.W, blk = blockIdx.x - g * a.W;
+    const int t = threadIdx.x, w = t >> 6;
+    uint32_t *ws = a.ws + (size_t)g * mb_words(a.W);
+    const uint32_t prefix = ws[256], pmask = ws[257];
+    __shared__ uint32_t hist[NW][256];
+    for (int i = t; i < NW * 256; i += MB_NT) (&hist[0][0])[i] = 0;
+    __syncthreads();
+    uint32_t key[MB_M];
+    const SelRows rows = mb_rows(a, g);
+    const int r0 = blk * MB_ROWS;
+    load_keys<MB_M, MB_NT>(rows, r0, key);
+    count_digits<MB_M, MB_NT>(key, r0, rows.n_total, prefix, pmask, shift, hist[w]);
+    __syncthreads();
+    if (t < 256) {
+        uint32_t s = 0;
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-        const int c = i * NW + w;
-        const int r = c * 64 + lane;
-        const bool valid = r < n_total;
-        const uint64_t gm = __ballot(valid && key[i] > tau);
-        const uint64_t em = __ballot(valid && key[i] == tau);
-        if (lane == 0 && c < nchunks)
-            chunk[c] = ((uint32_t)__popcll(gm) << 16) | (uint32_t)__popcll(em);
+        for (int v = 0; v < NW; ++v) s += hist[v][t];
+        if (s) atomicAdd(&ws[t], s);
+    }
+}
+
+// One wave per group: choose the digit of this pass, advance the state and
+// clear the histogram for the next pass.
+__global__ __launch_bounds__(64) void mb_pick_kernel(uint32_t *__restrict__ ws_all, int W, int shift) {
+    uint32_t *ws = ws_all + (size_t)blockIdx.x * mb_words(W);
+    const int lane = threadIdx.x;
+    uint4 c;
+    c.x = ws[252 - 4 * lane];
+    c.y = ws[253 - 4 * lane];
+    c.z = ws[254 - 4 * lane];
+    c.w = ws[255 - 4 * lane];
+    const uint32_t krem = ws[258];
+    uint32_t d, nk;
+    const bool mine = pick_digit(c, krem, &d, &nk);
+    for (int j = 0; j < 4; ++j) ws[252 - 4 * lane + j] = 0;  // each lane clears only the bins it read
+    if (mine) {
+        ws[256] |= d << shift;
+        ws[257] |= 0xFFu << shift;
+        ws[258] = nk;
+    }
+}
+
+// Per row block: how many keys are above tau and equal to it.
+__global__ __launch_bounds__(MB_NT) void mb_count_kernel(MbArgs a) {
+    const int g = blockIdx.x / a.W, blk = blockIdx.x - g * a.W;
+    const int t = threadIdx.x, lane = t & 63;
+    uint32_t *ws = a.ws + (size_t)g * mb_words(a.W);
+    const uint32_t tau = ws[256];
+    __shared__ uint32_t tot[2];
+    if (t < 2) tot[t] = 0;
+    __syncthreads();
+    uint32_t key[MB_M];
+    const SelRows rows = mb_rows(a, g);
+    const int r0 = blk * MB_ROWS;
+    load_keys<MB_M, MB_NT>(rows, r0, key);
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < MB_M; ++i) {
+        const int r = r0 + i * MB_NT + t;
+        const bool valid = r < rows.n_total;
+        gt += (uint32_t)__popcll(__ballot(valid && key[i] > tau));
+        eq += (uint32_t)__popcll(__ballot(valid && key[i] == tau));
+    }
+    if (lane == 0) {
+        atomicAdd(&tot[0], gt);
+        atomicAdd(&tot[1], eq);
     }
     __syncthreads();
-    if (w == 0) {
-        uint32_t a[4], local = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = 4 * lane + j;
-            a[j] = c < nchunks ? chunk[c] : 0u;
-            local += a[j];
-        }
-        uint32_t run = wave_prefix_incl(local) - local;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = 4 * lane + j;
-            if (c < nchunks) chunk[c] = run;
-            run += a[j];
-        }
+    if (t == 0) {
+        ws[260 + 2 * blk] = tot[0];
+        ws[260 + 2 * blk + 1] = tot[1];
     }
+}
+
+// Per row block: write the kept indices, offset by the counts of the blocks
+// before it.
+__global__ __launch_bounds__(MB_NT) void mb_write_kernel(MbArgs a, int32_t *__restrict__ keep_idx) {
+    const int g = blockIdx.x / a.W, blk = blockIdx.x - g * a.W;
+    const int t = threadIdx.x;
+    const uint32_t *ws = a.ws + (size_t)g * mb_words(a.W);
+    __shared__ uint32_t base[2];
+    __shared__ uint32_t chunk[MB_M * (MB_NT / 64)];
+    if (t < 2) {
+        uint32_t s = 0;
+        for (int b = 0; b < blk; ++b) s += ws[260 + 2 * b + t];
+        base[t] = s;
+    }
+    uint32_t key[MB_M];
+    const SelRows rows = mb_rows(a, g);
+    const int r0 = blk * MB_ROWS;
+    load_keys<MB_M, MB_NT>(rows, r0, key);
     __syncthreads();
-    const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-        const int c = i * NW + w;
-        const int r = c * 64 + lane;
-        const bool valid = r < n_total;
-        const uint64_t gm = __ballot(valid && key[i] > tau);
-        const uint64_t em = __ballot(valid && key[i] == tau);
-        if (valid) {
-            const uint32_t base = chunk[c];
-            const uint32_t gb = (base >> 16) + (uint32_t)__popcll(gm & below);
-            const uint32_t eb = (base & 0xFFFFu) + (uint32_t)__popcll(em & below);
-            // Exactly `budget` rows qualify, so every slot is below budget; the
-            // bound check only keeps a corrupt input from writing past the row.
-            uint32_t slot = 0xFFFFFFFFu;
-            if (key[i] > tau)
-                slot = gb + min(eb, quota);
-            else if (key[i] == tau && eb < quota)
-                slot = gb + eb;
-            if (slot < (uint32_t)budget) out[slot] = r;
-        }
-    }
+    write_kept<MB_M, MB_NT>(key, r0, rows.n_total, ws[256], ws[258], base[0], base[1],
+                            keep_idx + (size_t)g * a.budget, a.budget, chunk);
 }
 
 // ---------------------------------------------------------------------------
@@ -764,6 +928,13 @@ KVX_API int qf_score_keys(const void *k_new, kvx_shape shape, int64_t S, int32_t
     });
 }
 
+// Bytes of device workspace the multi-block selection needs (0 on chip).
+static int64_t select_workspace_bytes(int64_t G, int64_t n_total, int64_t budget) {
+    if (n_total <= KVX_ONCHIP_TOTAL || n_total <= budget) return 0;
+    const int64_t W = (n_total + MB_ROWS - 1) / MB_ROWS;
+    return G * (int64_t)mb_words((int)W) * 4;
+}
+
 KVX_API int kv_evict_workspace_size(kvx_shape shape, int64_t n_kept, int64_t S, kvx_evict_params p,
                                     size_t *bytes) {
     clear_error();
@@ -771,7 +942,7 @@ KVX_API int kv_evict_workspace_size(kvx_shape shape, int64_t n_kept, int64_t S, 
     int rc = validate_select_sizes(shape, n_kept, S, p, &G);
     if (rc) return rc;
     if (!bytes) return set_error(KVX_EINVAL, "kv_evict_workspace_size: NULL output");
-    *bytes = 0;
+    *bytes = (size_t)select_workspace_bytes(G, n_kept + S, p.budget);
     return KVX_OK;
 }
 
@@ -779,8 +950,6 @@ KVX_API int kv_evict_topk(const float *s_kept, const float *s_new, kvx_shape sha
                           int64_t S, kvx_evict_params p, int32_t *keep_idx, void *ws, size_t ws_bytes,
                           void *stream) {
     clear_error();
-    (void)ws;
-    (void)ws_bytes;
     int64_t G = 0;
     int rc = validate_select_sizes(shape, n_kept, S, p, &G);
     if (rc) return rc;
@@ -788,29 +957,44 @@ KVX_API int kv_evict_topk(const float *s_kept, const float *s_new, kvx_shape sha
     if (G == 0 || n_total == 0) return KVX_OK;
     if (!keep_idx || (n_kept > 0 && !s_kept) || (S > 0 && !s_new))
         return set_error(KVX_EINVAL, "kv_evict_topk: NULL buffer");
+    const int64_t need = select_workspace_bytes(G, n_total, p.budget);
+    if (need > 0 && (ws == nullptr || (int64_t)ws_bytes < need))
+        return set_error(KVX_EINVAL, "kv_evict_topk: n_total %lld needs a workspace of %lld bytes (got %zu)",
+                         (long long)n_total, (long long)need, ws ? ws_bytes : (size_t)0);
     hipStream_t st = (hipStream_t)stream;
     const int a = (int)n_kept, b = (int)S, bud = (int)p.budget, ns = (int)p.n_sink, rc2 = (int)p.recent;
     const int kl = p.keep == KVX_KEEP_LOW;
     const uint32_t grid = (uint32_t)G;
     constexpr int NT = KVX_SELECT_NT;
-    static_assert(NT == 256 || NT == 512 || NT == 1024, "selection block size");
-    // keys per thread: the smallest power of two covering n_total (<= KVX_MAX_TOTAL)
-    if (n_total <= NT)
-        select_kernel<1, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-    else if (n_total <= 2 * NT)
-        select_kernel<2, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-    else if (n_total <= 4 * NT)
-        select_kernel<4, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-    else if (n_total <= 8 * NT)
-        select_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-    else if (n_total <= 16 * NT)
-        select_kernel<16, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-    else if constexpr (KVX_MAX_TOTAL > 16 * NT) {
-        if (n_total <= 32 * NT)
-            select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+    static_assert(NT == 1024, "the on-chip bound assumes 1024-thread selection blocks");
+    static_assert(KVX_ONCHIP_TOTAL == 32 * NT, "keys per thread top out at 32");
+    if (need == 0) {
+        // keys per thread: the smallest power of two covering n_total (identity needs none)
+        if (n_total <= NT || n_total <= p.budget)
+            select_kernel<1, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        else if (n_total <= 2 * NT)
+            select_kernel<2, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        else if (n_total <= 4 * NT)
+            select_kernel<4, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        else if (n_total <= 8 * NT)
+            select_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        else if (n_total <= 16 * NT)
+            select_kernel<16, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
         else
-            select_kernel<64, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+            select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        return check_launch("kv_evict_topk");
     }
+    const int W = (int)((n_total + MB_ROWS - 1) / MB_ROWS);
+    if (G * W > INT32_MAX) return set_error(KVX_ERANGE, "kv_evict_topk: grid too large");
+    const MbArgs args{s_kept, s_new, a, b, bud, ns, rc2, kl, W, (uint32_t *)ws};
+    mb_init_kernel<<<grid, 256, 0, st>>>((uint32_t *)ws, W, bud);
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        mb_hist_kernel<<<(uint32_t)(G * W), MB_NT, 0, st>>>(args, shift);
+        mb_pick_kernel<<<grid, 64, 0, st>>>((uint32_t *)ws, W, shift);
+    }
+    mb_count_kernel<<<(uint32_t)(G * W), MB_NT, 0, st>>>(args);
+    mb_write_kernel<<<(uint32_t)(G * W), MB_NT, 0, st>>>(args, keep_idx);
     return check_launch("kv_evict_topk");
 }
 

@@ -140,6 +140,9 @@ SELECT_CASES = [
     (0, 8193, 8192, 4, 0, "high"), (8192, 8192, 8192, 4, 0, "high"), (8192, 8192, 8192, 4, 100, "low"),
     (0, 16384, 8192, 0, 0, "low"), (3, 5, 4, 1, 2, "high"), (0, 4097, 1, 0, 0, "low"),
     (100, 1949, 2000, 10, 30, "high"), (7, 77, 50, 49, 0, "low"),
+    # the on-chip bound (32 keys per thread) and the multi-block selection beyond it
+    (16384, 16384, 16384, 4, 0, "high"), (0, 40000, 20000, 4, 0, "low"), (20000, 20000, 20000, 4, 100, "high"),
+    (32768, 1, 32768, 4, 16, "low"), (70000, 30000, 70000, 0, 5, "low"),
 ]
 
 
@@ -152,8 +155,10 @@ def _select_gpu(sk, sn, n_kept, S, budget, n_sink, recent, keep):
         s_kept[:, :n_kept] = torch.from_numpy(sk).cuda()
     s_new = torch.from_numpy(np.ascontiguousarray(sn)).cuda() if S else torch.zeros((G, 1), device="cuda")
     idx = torch.full((G, budget), -7, dtype=torch.int32, device="cuda")
-    api.kv_evict_topk(s_kept, s_new, api.make_shape(1, 1, G, "bf16"), n_kept, S,
-                      api.make_params(budget, n_sink, recent, keep), idx)
+    shape, params = api.make_shape(1, 1, G, "bf16"), api.make_params(budget, n_sink, recent, keep)
+    need = api.kv_evict_workspace_size(shape, n_kept, S, params)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda") if need else None   # dirty on purpose
+    api.kv_evict_topk(s_kept, s_new, shape, n_kept, S, params, idx, ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy()
 
@@ -177,6 +182,46 @@ def test_select_matches_oracle(case, dist):
         want = oracle.select(s[g], budget, n_sink, recent, keep)
         assert np.array_equal(idx[g, :n_out], want), "group %d" % g
         assert np.all(idx[g, n_out:] == -7)                  # nothing written past n_out
+
+
+def test_multi_block_selection_checks_its_workspace():
+    import torch
+    api = _api()
+    from kv_cache_token_amd._lib import KvxError
+    G, S, budget = 2, 40000, 20000
+    shape, params = api.make_shape(1, 1, G, "bf16"), api.make_params(budget, 4, 0, "low")
+    need = api.kv_evict_workspace_size(shape, 0, S, params)
+    assert need == G * (260 + 2 * 3) * 4
+    assert api.kv_evict_workspace_size(shape, 0, 30000, params) == 0       # on chip
+    s = torch.zeros((G, S), device="cuda")
+    idx = torch.zeros((G, budget), dtype=torch.int32, device="cuda")
+    with pytest.raises(KvxError):
+        api.kv_evict_topk(None, s, shape, 0, S, params, idx, None)
+    with pytest.raises(KvxError):
+        api.kv_evict_topk(None, s, shape, 0, S, params, idx, torch.zeros(need - 4, dtype=torch.uint8, device="cuda"))
+
+
+def test_large_budget_stream_lockstep_with_oracle():
+    """Budget 20000 with 16384-token blocks: every call after the first selects
+    over more rows than fit on chip, through the multi-block path."""
+    import torch
+    from kv_cache_token_amd.cache import EvictingCache
+    G, S, budget, n_sink, recent = 3, 16384, 20000, 4, 64
+    c = EvictingCache(1, 1, G, budget, n_sink, recent, "low", "l2")
+    o = oracle.OracleCache(G, D, "bf16", budget, n_sink, recent, "low")
+    for blk in range(4):
+        K = synth.custom_keys((G, S, D), 1200 + blk, "bf16", kind="dup" if blk == 2 else "gauss")
+        V = synth.custom_keys((G, S, D), 1300 + blk, "bf16")
+        c.update(_t(K, "bf16"), _t(V, "bf16"))
+        o.update(K, V, scores_in=c.last_scores().cpu().numpy())
+    torch.cuda.synchronize()
+    k, v, s, p = c.kept()
+    for g in range(G):
+        ok, ov, os_, op = o.kept(g)
+        assert np.array_equal(p[g].cpu().numpy(), op)
+        assert np.array_equal(s[g].cpu().numpy(), os_)
+        assert np.array_equal(synth.torch_to_host(k[g], "bf16"), ok)
+        assert np.array_equal(synth.torch_to_host(v[g], "bf16"), ov)
 
 
 def test_select_real_infinities_rank_below_protected_rows():
