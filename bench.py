@@ -92,7 +92,7 @@ class Workload:
             keep = sc.keep if sc.mode == "l2" else "high"
             c = EvictingCache(cfg.L, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode,
                               f_mu if sc.filt == "mu" else None, sc.sign, cfg.dtype, stream=st,
-                              calib_tokens=cfg.calib_tokens)
+                              calib_tokens=cfg.calib_tokens, calib_keys=cfg.calib_keys)
             with torch.cuda.stream(st):
                 if sc.filt == "keysvd":       # freeze the fallback filters once, outside the timed step
                     c.update(*self.blocks[0])

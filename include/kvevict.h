@@ -260,6 +260,48 @@ KVX_API int qf_filters_from_keys(const void *k, int32_t dtype, int64_t G, int64_
                                  int64_t group_stride, int64_t D, float *out);
 
 /*
+ * kv_passthrough_append -- the fallback's pre-calibration passthrough
+ * (Q-Filters page, "How it works" step 2): until the key-SVD filter exists no
+ * row can be scored, so every row is kept, even over budget.  Copies the n_held
+ * held rows and then the S new rows of each group into the output, and writes
+ * their positions (row o gets position o: the passthrough only ever holds the
+ * stream's first tokens).
+ *   k_held, v_held  device [G, cap_held, D] of `shape.dtype`, n_held valid rows
+ *                   (may be NULL when n_held == 0)
+ *   k_new, v_new    device [G, S, D]
+ *   k_out, v_out    device [G, cap_out, D];  pos_out device [G, cap_out] int32
+ * Needs n_held <= cap_held and n_held + S <= cap_out.  When the outputs are the
+ * held buffers themselves (same pointers, cap_out == cap_held) only the new
+ * rows (and their positions) are written; any other overlap of an output with
+ * an input is rejected.  Asynchronous on `stream`.
+ * Errors: KVX_EINVAL (sizes, NULL, overlap), KVX_ERANGE, KVX_EDEVICE.
+ */
+KVX_API int kv_passthrough_append(const void *k_held, const void *v_held, int64_t n_held, int64_t cap_held,
+                                  const void *k_new, const void *v_new, int64_t S, kvx_shape shape, void *k_out,
+                                  void *v_out, int32_t *pos_out, int64_t cap_out, void *stream);
+
+/*
+ * qf_filters_from_keys_device -- the key-SVD fallback filter of
+ * qf_filters_from_keys, computed on the device and batched over G groups (one
+ * workgroup each; Q-Filters page, "Key-SVD fallback"): the column means of each
+ * group's first n keys are subtracted, the centred Gram matrix is accumulated in
+ * fp64 and its top eigenvector found by fp64 power iteration, stopped when no
+ * entry moves by 1e-14 on two successive steps; the entry of largest magnitude
+ * is made positive (lowest index on ties).
+ *   k        device keys of `dtype`; group g's row i at row g*group_stride + i
+ *   n        keys per group, 2 <= n <= KVX_MAX_TOTAL, group_stride >= n
+ *   D        64 or 128 (256 is KVX_ERANGE here; qf_filters_from_keys covers it)
+ *   out      device [G, D] float32, unit norm
+ *   status   device [G] int32: 0 converged; 1 still moving after max_iter steps
+ *            (top two eigenvalues too close to separate); 2 the centred keys
+ *            are all zero
+ * Asynchronous on `stream`; read `status` after synchronising.
+ * Errors: KVX_EINVAL, KVX_ERANGE, KVX_EDEVICE.
+ */
+KVX_API int qf_filters_from_keys_device(const void *k, int32_t dtype, int64_t G, int64_t n, int64_t group_stride,
+                                        int64_t D, float *out, int32_t *status, int32_t max_iter, void *stream);
+
+/*
  * kvx_stats -- byte accounting of a cache (Q-Filters page, "How it works",
  * last paragraph; L2Norm page, "How it works"): K+V bytes kept and the bytes a
  * full cache of tokens_seen rows would take, their ratio, and the filter bytes

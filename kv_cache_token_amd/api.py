@@ -169,6 +169,34 @@ def kv_evict_one_inplace(k_cache, v_cache, s_cache, pos_cache, k_new, v_new, s_n
     return _dispatch("kv_evict_one_inplace", args, prepare)
 
 
+def kv_passthrough_append(k_held, v_held, n_held: int, cap_held: int, k_new, v_new, S: int, shape: KvxShape,
+                          k_out, v_out, pos_out, cap_out: int, stream=None, prepare: bool = False):
+    """Pre-calibration passthrough: held rows then new rows into the output
+    (in place when the output is the held buffer)."""
+    torch = _torch()
+    G, td, Dd = _G(shape), torch_dtype(shape.dtype), shape.D
+    args = (_dev(k_held, "k_held", td, G * cap_held * Dd, allow_none=(n_held == 0)),
+            _dev(v_held, "v_held", td, G * cap_held * Dd, allow_none=(n_held == 0)), n_held, cap_held,
+            _dev(k_new, "k_new", td, G * S * Dd, allow_none=(S == 0)),
+            _dev(v_new, "v_new", td, G * S * Dd, allow_none=(S == 0)), S, shape,
+            _dev(k_out, "k_out", td, G * cap_out * Dd), _dev(v_out, "v_out", td, G * cap_out * Dd),
+            _dev(pos_out, "pos_out", torch.int32, G * cap_out), cap_out, _stream(stream))
+    return _dispatch("kv_passthrough_append", args, prepare)
+
+
+def qf_filters_from_keys_device(k, G: int, n: int, group_stride: int, out, status, max_iter: int = 20000,
+                                stream=None, prepare: bool = False):
+    """Key-SVD fallback filters of G groups on the device: out [G, D] float32,
+    status [G] int32 (0 converged, 1 not separated within max_iter, 2 zero)."""
+    torch = _torch()
+    code = dtype_code(k.dtype)
+    Dd = k.shape[-1]
+    args = (_dev(k, "k", torch_dtype(code), (G - 1) * group_stride * Dd + n * Dd if G else 0), code, G, n,
+            group_stride, Dd, _dev(out, "out", torch.float32, G * Dd), _dev(status, "status", torch.int32, G),
+            max_iter, _stream(stream))
+    return _dispatch("qf_filters_from_keys_device", args, prepare)
+
+
 # --------------------------------------------------------------------------- host
 
 

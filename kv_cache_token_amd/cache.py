@@ -21,7 +21,8 @@ D = api.D
 class EvictingCache:
     def __init__(self, L: int, B: int, H: int, budget: int, n_sink: int = 4, recent: int = 0,
                  keep: str = "low", mode: str = "l2", filters=None, sign: int = 1, dtype: str = "bf16",
-                 device="cuda", calib_tokens: int = 0, stream=None, head_dim: int = 128):
+                 device="cuda", calib_tokens: int = 0, stream=None, head_dim: int = 128,
+                 calib_keys: str = "crossing", calib_max_iter: int = 20000):
         import torch
         self.L, self.B, self.H, self.G = L, B, H, L * B * H
         self.budget, self.n_sink, self.recent = budget, n_sink, recent
@@ -32,12 +33,20 @@ class EvictingCache:
         self.shape = api.make_shape(L, B, H, dtype, head_dim)
         self.params = api.make_params(budget, n_sink, recent, self.keep)
         self.calib_tokens = calib_tokens
+        self.calib_keys = calib_keys
+        self.calib_max_iter = calib_max_iter
         self.stream = stream
         self.device = torch.device(device)
+        if calib_keys not in ("crossing", "first"):
+            raise ValueError("calib_keys must be 'crossing' or 'first'")
+        if mode == "proj" and filters is None:
+            if calib_tokens < 2:
+                raise ValueError("projection needs filters or calib_tokens >= 2 (key-SVD fallback)")
+            if head_dim not in (64, 128):
+                raise ValueError("the key-SVD fallback estimates filters on the device for head dims 64 "
+                                 "and 128; pass filters for head dim %d" % head_dim)
         if mode not in ("l2", "proj"):
             raise ValueError("mode must be 'l2' or 'proj'")
-        if mode == "proj" and filters is None and calib_tokens <= 0:
-            raise ValueError("projection needs filters or calib_tokens > 0 (key-SVD fallback)")
         if n_sink + recent >= budget:
             raise ValueError("n_sink + recent must be below budget")
         if mode == "proj" and sign not in (1, -1):
@@ -61,6 +70,8 @@ class EvictingCache:
             self.set_filters(filters)
         self.n_kept = 0
         self.tokens_seen = 0
+        self._held = None          # pre-calibration rows (k, v, pos) [G, calib_tokens - 1, *]
+        self.calib_status = None   # [G] int32 of the last fallback estimate
 
     # -- filters -----------------------------------------------------------
     def set_filters(self, filters, per_group: bool = False) -> None:
@@ -77,19 +88,75 @@ class EvictingCache:
             self.score_shape = self.shape
         self.filters = f.to(self.device).contiguous()
 
-    def _freeze_fallback(self, k_new) -> None:
-        S = k_new.shape[1]
-        if self.tokens_seen != 0 or S < self.calib_tokens:
-            raise NotImplementedError("key-SVD fallback: the first block must hold at least calib_tokens "
-                                      "rows (the pre-calibration passthrough is not implemented)")
+    @property
+    def calibrating(self) -> bool:
+        """True while the key-SVD fallback filter has not been frozen yet."""
+        return self.mode == "proj" and self.filters is None
+
+    def _passthrough(self, k_new, v_new, S: int, prepare: bool):
+        """Hold the block unscored (Q-Filters page, "How it works" step 2: with
+        no filter there is no eviction, even over budget)."""
         import torch
-        first = k_new[:, :self.calib_tokens].contiguous().cpu()
-        if first.dtype in (torch.bfloat16, torch.float16):
-            host = first.view(torch.int16).numpy().view(np.uint16)
+        cap = self.calib_tokens - 1
+        if self._held is None:
+            td = api.torch_dtype(self.shape.dtype)
+            self._held = (torch.empty((self.G, cap, self.D), dtype=td, device=self.device),
+                          torch.empty((self.G, cap, self.D), dtype=td, device=self.device),
+                          torch.empty((self.G, cap), dtype=torch.int32, device=self.device))
+        hk, hv, hp = self._held
+        call = api.kv_passthrough_append(hk, hv, self.n_kept, cap, k_new, v_new, S, self.shape, hk, hv, hp, cap,
+                                         self.stream, prepare=prepare)
+        self.n_kept += S
+        self.tokens_seen += S
+        return [call] if prepare else []
+
+    def _crossing(self, k_new, v_new, S: int, prepare: bool):
+        """The block that brings the tokens seen to calib_tokens: estimate every
+        group's filter from the keys held so far plus this block (all of them,
+        or with calib_keys="first" the first calib_tokens), freeze it, then run
+        the step over the whole concatenation from an empty cache, so that every
+        held row is scored with the frozen filter (Q-Filters page, "How it
+        works" step 2, "Key-SVD fallback", "Path dependence")."""
+        import torch
+        calls = []
+        n_held, n_total = self.n_kept, self.n_kept + S
+        if n_held == 0:
+            bk, bv, extra = k_new, v_new, ()
         else:
-            host = first.numpy()
-        dt = "f16" if first.dtype == torch.float16 else "bf16"
-        self.set_filters(api.qf_filters_from_keys(host, self.calib_tokens, dt), per_group=True)
+            td = api.torch_dtype(self.shape.dtype)
+            bk = torch.empty((self.G, n_total, self.D), dtype=td, device=self.device)
+            bv = torch.empty_like(bk)
+            bp = torch.empty((self.G, n_total), dtype=torch.int32, device=self.device)
+            hk, hv, _ = self._held
+            extra = self._held + (bp,)
+            calls.append(api.kv_passthrough_append(hk, hv, n_held, self.calib_tokens - 1, k_new, v_new, S,
+                                                   self.shape, bk, bv, bp, n_total, self.stream, prepare=prepare))
+        n_calib = n_total if self.calib_keys == "crossing" else self.calib_tokens
+        f = torch.empty((self.G, self.D), dtype=torch.float32, device=self.device)
+        self.calib_status = torch.empty(self.G, dtype=torch.int32, device=self.device)
+        calls.append(api.qf_filters_from_keys_device(bk, self.G, n_calib, n_total, f, self.calib_status,
+                                                     self.calib_max_iter, self.stream, prepare=prepare))
+        self.set_filters(f, per_group=True)
+        if not prepare:
+            self.check_calibration()
+        self._held = None
+        self.n_kept, self.tokens_seen = 0, 0
+        more, refs = self._step(bk, bv, prepare)
+        return calls + more, (bk, bv, f, self.calib_status) + extra + tuple(refs)
+
+    def check_calibration(self) -> None:
+        """Wait for the last fallback estimate and raise if a group has no
+        dominant key direction (status 1: top two eigenvalues not separated;
+        2: its centred keys are all zero)."""
+        import torch
+        if self.calib_status is None:
+            return
+        torch.cuda.synchronize(self.device)
+        st = self.calib_status.cpu().numpy()
+        bad = np.flatnonzero(st)
+        if bad.size:
+            raise RuntimeError("key-SVD fallback: %d group(s) have no dominant key direction (first: group %d, "
+                               "status %d)" % (bad.size, int(bad[0]), int(st[bad[0]])))
 
     # -- state -------------------------------------------------------------
     @property
@@ -101,8 +168,16 @@ class EvictingCache:
         return self._bufs[self._cur]
 
     def kept(self):
-        k, v, s, p = self._bufs[self._cur]
+        """Views (k, v, s, pos) of the kept rows; before the fallback filter is
+        frozen the held rows, with s None (they are not scored yet)."""
         n = self.n_kept
+        if self.calibrating:
+            if self._held is None:
+                k, v, _, p = self._bufs[self._cur]
+                return k[:, :0], v[:, :0], None, p[:, :0]
+            hk, hv, hp = self._held
+            return hk[:, :n], hv[:, :n], None, hp[:, :n]
+        k, v, s, p = self._bufs[self._cur]
         return k[:, :n], v[:, :n], s[:, :n], p[:, :n]
 
     def last_scores(self):
@@ -114,6 +189,7 @@ class EvictingCache:
         keys) are forgotten unless keep_filters is set."""
         self.n_kept = 0
         self.tokens_seen = 0
+        self._held = None
         if not keep_filters and self.mode == "proj" and self.calib_tokens > 0 and self.score_shape is not self.shape:
             self.filters = None
 
@@ -149,10 +225,11 @@ class EvictingCache:
         calls = []
         if S == 0:
             return calls, (k_new, v_new)
-        if self.mode == "proj" and self.filters is None:
-            if prepare:
-                raise RuntimeError("freeze the fallback filters (one update) before planning")
-            self._freeze_fallback(k_new)
+        if self.calibrating:
+            if self.tokens_seen + S < self.calib_tokens:
+                calls = self._passthrough(k_new, v_new, S, prepare)
+                return calls, (k_new, v_new) + self._held
+            return self._crossing(k_new, v_new, S, prepare)
         s_new = self._scores(S)
         calls.append(api.qf_score_keys(k_new, self.score_shape, S, self.mode, self.filters, self.sign, s_new,
                                        self.stream, prepare=prepare))
@@ -183,9 +260,14 @@ class EvictingCache:
         buffers before each replay).  The plan replays the calls with no
         per-call marshalling (or inside a captured HIP graph) and keeps the
         tensors it points at alive.  The cache's bookkeeping is left at the
-        plan's starting state."""
+        plan's starting state.  A stream that starts a key-SVD fallback cache
+        records the passthrough and the estimate as well; the filters are then
+        frozen to a buffer the plan writes when it runs (StreamPlan.check reads
+        the estimate's status)."""
         start = (self.n_kept, self.tokens_seen, self._cur) if keep_state else (0, 0, 0)
         self.n_kept, self.tokens_seen, self._cur = start
+        if not keep_state:
+            self._held = None
         calls, keep = [], []
         for k, v in blocks:
             c, refs = self._step(k, v, prepare=True)
@@ -201,6 +283,10 @@ class StreamPlan:
 
     def __init__(self, cache: EvictingCache, calls, start, final, keepalive):
         self.cache, self.calls, self.start, self.final, self._keep = cache, calls, start, final, keepalive
+
+    def check(self) -> None:
+        """After run(): wait and raise if a fallback estimate the plan made failed."""
+        self.cache.check_calibration()
 
     @property
     def names(self):

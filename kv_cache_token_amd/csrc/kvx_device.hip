@@ -778,6 +778,284 @@ __global__ __launch_bounds__(KVX_DECODE_BLOCK) void evict_one_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Pre-calibration passthrough ("Q-Filters — Query-Agnostic Projection
+// Eviction", "How it works" step 2): before the fallback filter exists every
+// row is kept.  out[g, o] = held[g, o] for o < n_held, new[g, o - n_held] after
+// that, positions o (the passthrough only happens from token 0).  When the
+// output is the held buffer itself only the new rows are written.
+// ---------------------------------------------------------------------------
+template <int DT, int HD>
+__global__ __launch_bounds__(256) void append_rows_kernel(const char *__restrict__ k_held,
+                                                          const char *__restrict__ v_held, int64_t cap_held,
+                                                          int64_t n_held, const char *__restrict__ k_new,
+                                                          const char *__restrict__ v_new, int64_t S, char *k_out,
+                                                          char *v_out, int32_t *pos_out, int64_t cap_out,
+                                                          int64_t first, int64_t G) {
+    using R = Row<DT, HD>;
+    const int64_t rows = n_held + S - first;  // rows written per group
+    const int64_t total = G * rows * R::kLanes;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int part = (int)(e % R::kLanes);
+        const int64_t gr = e / R::kLanes, g = gr / rows, o = first + gr % rows;
+        const char *ks, *vs;
+        if (o < n_held) {
+            ks = k_held + ((size_t)g * cap_held + o) * R::kBytes;
+            vs = v_held + ((size_t)g * cap_held + o) * R::kBytes;
+        } else {
+            ks = k_new + ((size_t)g * S + (o - n_held)) * R::kBytes;
+            vs = v_new + ((size_t)g * S + (o - n_held)) * R::kBytes;
+        }
+        const size_t od = ((size_t)g * cap_out + o) * R::kBytes + part * 16;
+        st16(k_out + od, ld16(ks + part * 16));
+        st16(v_out + od, ld16(vs + part * 16));
+        if (part == 0) pos_out[(size_t)g * cap_out + o] = (int32_t)o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Key-SVD fallback filters on the device ("Q-Filters — Query-Agnostic
+// Projection Eviction", "Key-SVD fallback"): per group, the top right singular
+// vector of its first n keys after subtracting their column means, i.e. the
+// top eigenvector of the centred Gram matrix C = Xc^T Xc, signed so that its
+// largest-magnitude entry is positive (lowest index on ties).
+// One workgroup per group, all in fp64: a pass over the keys for the column
+// means, a pass that stages chunks of centred rows in LDS and accumulates C in
+// 8 x 8 register tiles (one per thread), then power iteration on C held in
+// registers until the vector stops moving.
+// ---------------------------------------------------------------------------
+template <int HD>
+struct FbLayout {
+    static constexpr int T = 8;             // Gram tile edge per thread
+    static constexpr int TPR = HD / T;      // threads along one tile row
+    static constexpr int NT = TPR * TPR;    // 64 threads for HD 64, 256 for HD 128
+    static constexpr int CH = 4096 / HD;    // staged rows per chunk (32 KB of fp64)
+    static_assert(NT >= 64 && NT <= 256, "device fallback estimator covers head dims 64 and 128");
+};
+
+__device__ __forceinline__ double shfl_xor_f64(double x, int off) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+    const uint32_t lo = __shfl_xor((uint32_t)u, off), hi = __shfl_xor((uint32_t)(u >> 32), off);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+template <int DT, int HD>
+__global__ __launch_bounds__(FbLayout<HD>::NT) void fallback_filter_kernel(
+    const char *__restrict__ k, int64_t group_stride, int64_t n, float *__restrict__ out,
+    int32_t *__restrict__ status, int max_iter) {
+    using L = FbLayout<HD>;
+    using R = Row<DT, HD>;
+    constexpr int NT = L::NT, TPR = L::TPR, CH = L::CH, E = R::kElemsPerLane, SLOTS = NT / R::kLanes;
+    static_assert(SLOTS >= 1 && NT % R::kLanes == 0, "a workgroup covers whole rows");
+    __shared__ double xd[CH * HD];  // staged centred rows; first the column partial sums
+    __shared__ double mu[HD], v[HD], y[HD], lam[2];
+    __shared__ int flag;
+    const int t = threadIdx.x, lane = t & 63;
+    const int64_t g = blockIdx.x;
+    const char *kg = k + (size_t)g * group_stride * R::kBytes;
+
+    // column means: thread (slot, part) sums rows slot, slot + SLOTS, ...
+    {
+        const int part = t % R::kLanes, slot = t / R::kLanes;
+        double acc[E];
+#pragma unroll
+        for (int q = 0; q < E; ++q) acc[q] = 0.0;
+        for (int64_t r = slot; r < n; r += SLOTS) {
+            float x[E];
+            widen<DT>(ld16(kg + (size_t)r * R::kBytes + part * 16), x);
+#pragma unroll
+            for (int q = 0; q < E; ++q) acc[q] += (double)x[q];
+        }
+#pragma unroll
+        for (int q = 0; q < E; ++q) xd[slot * HD + part * E + q] = acc[q];
+        __syncthreads();
+        for (int c = t; c < HD; c += NT) {
+            double s = 0.0;
+            for (int j = 0; j < SLOTS; ++j) s += xd[j * HD + c];
+            mu[c] = s / (double)n;
+        }
+        __syncthreads();
+    }
+
+    // centred Gram matrix, tile (r0.., c0..) of 8 x 8 per thread
+    const int tr = t / TPR, tc = t % TPR, r0 = tr * L::T, c0 = tc * L::T;
+    double C[L::T][L::T];
+#pragma unroll
+    for (int i = 0; i < L::T; ++i)
+#pragma unroll
+        for (int j = 0; j < L::T; ++j) C[i][j] = 0.0;
+    for (int64_t base = 0; base < n; base += CH) {
+        const int rows = (int)min((int64_t)CH, n - base);
+        for (int e = t; e < rows * R::kLanes; e += NT) {
+            const int r = e / R::kLanes, part = e % R::kLanes;
+            float x[E];
+            widen<DT>(ld16(kg + (size_t)(base + r) * R::kBytes + part * 16), x);
+#pragma unroll
+            for (int q = 0; q < E; ++q) xd[r * HD + part * E + q] = (double)x[q] - mu[part * E + q];
+        }
+        __syncthreads();
+        for (int r = 0; r < rows; ++r) {
+            double a[L::T], b[L::T];
+#pragma unroll
+            for (int i = 0; i < L::T; ++i) {
+                a[i] = xd[r * HD + r0 + i];
+                b[i] = xd[r * HD + c0 + i];
+            }
+#pragma unroll
+            for (int i = 0; i < L::T; ++i)
+#pragma unroll
+                for (int j = 0; j < L::T; ++j) C[i][j] = __builtin_fma(a[i], b[j], C[i][j]);
+        }
+        __syncthreads();
+    }
+
+    // y = C x over the register tiles (x, y in LDS); ends with a barrier
+    auto matvec = [&](const double *x, double *yv) {
+        double p[L::T];
+#pragma unroll
+        for (int i = 0; i < L::T; ++i) {
+            double s = 0.0;
+#pragma unroll
+            for (int j = 0; j < L::T; ++j) s = __builtin_fma(C[i][j], x[c0 + j], s);
+            p[i] = s;
+        }
+#pragma unroll
+        for (int off = TPR / 2; off > 0; off >>= 1)
+#pragma unroll
+            for (int i = 0; i < L::T; ++i) p[i] += shfl_xor_f64(p[i], off);
+        if (tc == 0)
+#pragma unroll
+            for (int i = 0; i < L::T; ++i) yv[r0 + i] = p[i];
+        __syncthreads();
+    };
+    // wave-0 helpers over HD-long LDS vectors
+    auto wsum = [&](double s) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s += shfl_xor_f64(s, off);
+        return s;
+    };
+    auto wmax = [&](double s) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s = fmax(s, shfl_xor_f64(s, off));
+        return s;
+    };
+    // x <- y / |y| (after removing the component along `away` when given);
+    // returns 2 for a zero y, 1 when no entry of x moved by 1e-14, else 0
+    auto renorm = [&](double *x, double *yv, const double *away) {
+        if (away) {
+            double d = 0.0;
+            for (int i = lane; i < HD; i += 64) d += away[i] * yv[i];
+            d = wsum(d);
+            for (int i = lane; i < HD; i += 64) yv[i] -= d * away[i];
+        }
+        double ss = 0.0;
+        for (int i = lane; i < HD; i += 64) ss += yv[i] * yv[i];
+        ss = wsum(ss);
+        const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+        double dmax = 0.0;
+        for (int i = lane; i < HD; i += 64) {
+            const double nv = yv[i] * inv;
+            dmax = fmax(dmax, fabs(nv - x[i]));
+            x[i] = nv;
+        }
+        dmax = wmax(dmax);
+        return !(ss > 0.0) ? 2 : (dmax < 1e-14 ? 1 : 0);
+    };
+    auto start = [&](double *x, uint32_t salt) {
+        for (int i = t; i < HD; i += NT) {
+            const uint32_t h = ((uint32_t)(i + 1) ^ salt) * 2654435761u;
+            x[i] = ((h >> 31) ? -1.0 : 1.0) * (0.5 + (double)((h >> 8) & 0xFFFF) / 65536.0);
+        }
+    };
+    // power iteration from a fixed, generic start vector; `flag` carries wave
+    // 0's verdict to the workgroup
+    start(v, 0u);
+    __syncthreads();
+    int calm = 0, it = 0, f = 0;
+    for (; it < max_iter; ++it) {
+        matvec(v, y);
+        if (t < 64) {
+            const int r = renorm(v, y, nullptr);
+            if (lane == 0) flag = r;
+        }
+        __syncthreads();
+        f = flag;
+        __syncthreads();  // every thread has read flag before wave 0 rewrites it
+        if (f == 2) break;
+        calm = f == 1 ? calm + 1 : 0;
+        if (calm >= 2) break;
+    }
+    int st = f == 2 ? 2 : (calm >= 2 ? 0 : 1);
+    if (st == 0) {
+        // Separation check: the top eigenvalue must be unique.  lambda1 is the
+        // Rayleigh quotient of v; lambda2 is approached from below by power
+        // iteration restricted to the complement of v (w is kept orthogonal to
+        // v), for at most as many steps again.  Equal top eigenvalues (to 1e-9
+        // relative) are reported like a failure to converge.
+        matvec(v, y);
+        double *w = mu;  // the means are no longer needed
+        if (t < 64) {
+            double l1 = 0.0;
+            for (int i = lane; i < HD; i += 64) l1 += v[i] * y[i];
+            l1 = wsum(l1);
+            if (lane == 0) lam[0] = l1;
+        }
+        start(w, 0x9E3779B9u);
+        __syncthreads();
+        if (t < 64) renorm(w, w, v);  // orthogonalise and normalise the start (w's movement is ignored)
+        __syncthreads();
+        int calm2 = 0;
+        for (int it2 = 0; it2 < it + 64; ++it2) {
+            matvec(w, y);
+            if (t < 64) {
+                double l2 = 0.0;
+                for (int i = lane; i < HD; i += 64) l2 += w[i] * y[i];
+                l2 = wsum(l2);
+                const int r = renorm(w, y, v);
+                if (lane == 0) {
+                    lam[1] = l2;
+                    flag = r;
+                }
+            }
+            __syncthreads();
+            const int f2 = flag;
+            const bool tied = lam[1] >= lam[0] * (1.0 - 1e-9);
+            __syncthreads();
+            if (tied) {
+                st = 1;
+                break;
+            }
+            if (f2 == 2) break;  // nothing outside v: rank one
+            calm2 = f2 == 1 ? calm2 + 1 : 0;
+            if (calm2 >= 2) break;
+        }
+    }
+    if (t < 64) {
+        double best = -1.0;
+        int bi = HD;
+        for (int i = lane; i < HD; i += 64) {
+            const double m = fabs(v[i]);
+            if (m > best) {
+                best = m;
+                bi = i;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const double ob = shfl_xor_f64(best, off);
+            const int oi = __shfl_xor(bi, off);
+            if (ob > best || (ob == best && oi < bi)) {
+                best = ob;
+                bi = oi;
+            }
+        }
+        const double sg = v[bi] > 0.0 ? 1.0 : -1.0;
+        for (int i = lane; i < HD; i += 64) out[(size_t)g * HD + i] = (float)(sg * v[i]);
+        if (lane == 0) status[g] = st;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side validation shared by the entry points.
 // ---------------------------------------------------------------------------
 int check_shape(const kvx_shape &sh, int64_t *G) {
@@ -1059,6 +1337,78 @@ KVX_API int kv_evict_one_inplace(void *k_cache, void *v_cache, float *s_cache, i
         return 0;
     });
     return check_launch("kv_evict_one_inplace");
+}
+
+KVX_API int kv_passthrough_append(const void *k_held, const void *v_held, int64_t n_held, int64_t cap_held,
+                                  const void *k_new, const void *v_new, int64_t S, kvx_shape shape, void *k_out,
+                                  void *v_out, int32_t *pos_out, int64_t cap_out, void *stream) {
+    clear_error();
+    int64_t G = 0;
+    int rc = check_shape(shape, &G);
+    if (rc) return rc;
+    if (n_held < 0 || S < 0 || cap_held < 0 || cap_out < 0 || n_held > cap_held || n_held + S > cap_out)
+        return set_error(KVX_EINVAL, "kv_passthrough_append: need 0 <= n_held <= cap_held and n_held + S <= cap_out "
+                         "(n_held %lld, cap_held %lld, S %lld, cap_out %lld)", (long long)n_held, (long long)cap_held,
+                         (long long)S, (long long)cap_out);
+    if (n_held + S > INT32_MAX) return set_error(KVX_ERANGE, "kv_passthrough_append: positions beyond int32");
+    if (G == 0 || n_held + S == 0) return KVX_OK;
+    if (!k_out || !v_out || !pos_out || (S > 0 && (!k_new || !v_new)) || (n_held > 0 && (!k_held || !v_held)))
+        return set_error(KVX_EINVAL, "kv_passthrough_append: NULL buffer");
+    const size_t row = (size_t)shape.D * (shape.dtype == KVX_F32 ? 4 : 2);
+    const bool alias = k_out == k_held && v_out == v_held && cap_out == cap_held;
+    auto overlap = [](const void *a, size_t na, const void *b, size_t nb) {
+        const char *x = (const char *)a, *y = (const char *)b;
+        return a && b && na && nb && x < y + nb && y < x + na;
+    };
+    const size_t out_b = (size_t)G * cap_out * row, held_b = (size_t)G * cap_held * row,
+                 new_b = (size_t)G * S * row;
+    if (!alias && n_held > 0 &&
+        (overlap(k_out, out_b, k_held, held_b) || overlap(k_out, out_b, v_held, held_b) ||
+         overlap(v_out, out_b, k_held, held_b) || overlap(v_out, out_b, v_held, held_b)))
+        return set_error(KVX_EINVAL, "kv_passthrough_append: output overlaps the held rows without being them");
+    if (overlap(k_out, out_b, k_new, new_b) || overlap(k_out, out_b, v_new, new_b) ||
+        overlap(v_out, out_b, k_new, new_b) || overlap(v_out, out_b, v_new, new_b) ||
+        overlap(k_out, out_b, v_out, out_b))
+        return set_error(KVX_EINVAL, "kv_passthrough_append: output overlaps the new rows or itself");
+    const int64_t first = alias ? n_held : 0;
+    const int64_t lanes = G * (n_held + S - first) * (int64_t)(row / 16);
+    if (lanes == 0) return KVX_OK;
+    const uint32_t grid = (uint32_t)std::min<int64_t>((lanes + 255) / 256, 65536);
+    hipStream_t st = (hipStream_t)stream;
+    dispatch_row(shape, true, [&](auto dt, auto hd) {
+        append_rows_kernel<decltype(dt)::value, decltype(hd)::value><<<grid, 256, 0, st>>>(
+            (const char *)k_held, (const char *)v_held, cap_held, n_held, (const char *)k_new, (const char *)v_new,
+            S, (char *)k_out, (char *)v_out, pos_out, cap_out, first, G);
+        return 0;
+    });
+    return check_launch("kv_passthrough_append");
+}
+
+KVX_API int qf_filters_from_keys_device(const void *k, int32_t dtype, int64_t G, int64_t n, int64_t group_stride,
+                                        int64_t D, float *out, int32_t *status, int32_t max_iter, void *stream) {
+    clear_error();
+    if (G < 0 || n < 2 || n > KVX_MAX_TOTAL || group_stride < n || max_iter < 1)
+        return set_error(KVX_EINVAL, "qf_filters_from_keys_device: need G >= 0, 2 <= n <= %d, group_stride >= n, "
+                         "max_iter >= 1 (n %lld, group_stride %lld, max_iter %d)", KVX_MAX_TOTAL, (long long)n,
+                         (long long)group_stride, (int)max_iter);
+    if (D != 64 && D != 128)
+        return set_error(KVX_ERANGE, "qf_filters_from_keys_device: head dim %lld (64 or 128 on the device)",
+                         (long long)D);
+    if (dtype != KVX_BF16 && dtype != KVX_F16 && dtype != KVX_F32)
+        return set_error(KVX_EINVAL, "qf_filters_from_keys_device: bad dtype %d", (int)dtype);
+    if (G == 0) return KVX_OK;
+    if (!k || !out || !status) return set_error(KVX_EINVAL, "qf_filters_from_keys_device: NULL buffer");
+    if (G > INT32_MAX) return set_error(KVX_ERANGE, "qf_filters_from_keys_device: too many groups");
+    const kvx_shape sh{1, 1, 1, D, dtype};
+    hipStream_t st = (hipStream_t)stream;
+    dispatch_row(sh, false, [&](auto dt, auto hd) {
+        constexpr int HD = decltype(hd)::value;
+        if constexpr (HD <= 128)
+            fallback_filter_kernel<decltype(dt)::value, HD><<<(uint32_t)G, FbLayout<HD>::NT, 0, st>>>(
+                (const char *)k, group_stride, n, out, status, (int)max_iter);
+        return 0;
+    });
+    return check_launch("qf_filters_from_keys_device");
 }
 
 }  // extern "C"

@@ -68,6 +68,7 @@ class Config:
     recent: int
     scorers: Tuple[Scorer, ...]
     calib_tokens: int = 0
+    calib_keys: str = "crossing"   # fallback estimate from the whole crossing block, or the "first" calib_tokens
 
     @property
     def G(self) -> int:
@@ -94,7 +95,7 @@ CONFIGS = {
     4: Config(4, "c4_chunked_prefill_32k", 28, 1, 8, "bf16", "aniso", (4096,) * 8, 4096, 4, 0,
               (Scorer("l2", "low"), Scorer("proj", "high", -1, "mu"))),
     5: Config(5, "c5_keysvd_fallback_128k", 32, 1, 8, "bf16", "aniso", (8192,) * 16, 8192, 4, 0,
-              (Scorer("proj", "high", +1, "keysvd"),), calib_tokens=128),
+              (Scorer("proj", "high", +1, "keysvd"),), calib_tokens=128, calib_keys="first"),
 }
 
 

@@ -9,7 +9,9 @@ method's arithmetic.
 The eviction rules live in ``kvx_oracle.c`` (plain C, fp64 scoring, a plain sort
 for the ranking); this module loads it with ctypes, building it with gcc if the
 shared object is absent.  The calibration rules (query-SVD filter, GQA averaging,
-key-SVD fallback) live in ``calib.py`` and use numpy's SVD.
+key-SVD fallback) live in ``calib.py`` and use numpy's SVD; ``FallbackOracleCache``
+composes the fallback estimate with the step in the lifecycle the Q-Filters page
+describes (passthrough below calib_tokens, freeze at the crossing block).
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against
 brute force, closed forms, an independent streaming implementation and the
@@ -159,3 +161,80 @@ class OracleCache:
         c = OracleCache.__new__(OracleCache)
         c.__dict__.update({k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in self.__dict__.items()})
         return c
+
+
+def _widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of float32 keys or of bf16 / fp16 bit patterns."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    bits = np.asarray(x, dtype=np.uint16)
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class FallbackOracleCache:
+    """The key-SVD fallback lifecycle of one cache of G groups (Q-Filters page,
+    "How it works" step 2, "Key-SVD fallback", "Path dependence").
+
+    * Before any filter exists nothing can be scored, so every row is held:
+      the cache keeps all of its tokens, even over budget.
+    * The block that brings the tokens seen to calib_tokens freezes the filter
+      of each group: ``estimate_filter_dir`` (calib.py) over the held keys plus
+      that block's keys (calib_keys="crossing"; different chunkings therefore
+      freeze different filters), or over exactly the first calib_tokens keys
+      (calib_keys="first").  The filter is stored as float32.
+    * The same call then scores every held row and the block's rows with the
+      frozen filter and runs the eviction step over the whole concatenation
+      from an empty cache; later blocks are ordinary steps (OracleCache).
+
+    ``filters_in`` replaces the estimate (lockstep runs), ``scores_in`` the
+    scores of the crossing call's concatenation or of an ordinary block."""
+
+    def __init__(self, G: int, D: int, dtype: str, budget: int, n_sink: int, recent: int, calib_tokens: int,
+                 sign: int = 1, calib_keys: str = "crossing"):
+        if calib_tokens < 2 or calib_keys not in ("crossing", "first"):
+            raise OracleError("calib_tokens >= 2 and calib_keys in {crossing, first} required")
+        self.G, self.D, self.dtype = G, D, dtype
+        self.budget, self.n_sink, self.recent, self.sign = budget, n_sink, recent, sign
+        self.calib_tokens, self.calib_keys = calib_tokens, calib_keys
+        npdt = np.float32 if dtype == "f32" else np.uint16
+        self.held_k = np.zeros((G, 0, D), dtype=npdt)
+        self.held_v = np.zeros((G, 0, D), dtype=npdt)
+        self.filters = None
+        self.inner: Optional[OracleCache] = None
+        self.crossing_rows = 0
+
+    @property
+    def tokens(self) -> int:
+        return int(self.inner.tokens[0]) if self.inner is not None else self.held_k.shape[1]
+
+    def update(self, k_new: np.ndarray, v_new: np.ndarray, scores_in: Optional[np.ndarray] = None,
+               filters_in: Optional[np.ndarray] = None):
+        if self.inner is not None:
+            self.inner.update(k_new, v_new, scores_in)
+            return
+        k_all = np.concatenate([self.held_k, np.asarray(k_new)], axis=1)
+        v_all = np.concatenate([self.held_v, np.asarray(v_new)], axis=1)
+        n = k_all.shape[1]
+        if n < self.calib_tokens:
+            self.held_k, self.held_v = k_all, v_all
+            return
+        if filters_in is None:
+            m = n if self.calib_keys == "crossing" else self.calib_tokens
+            f = np.stack([calib.estimate_filter_dir(_widen(k_all[g, :m], self.dtype)) for g in range(self.G)])
+            self.filters = f.astype(np.float32)
+        else:
+            self.filters = np.ascontiguousarray(np.asarray(filters_in, dtype=np.float32).reshape(self.G, self.D))
+        self.crossing_rows = n
+        self.inner = OracleCache(self.G, self.D, self.dtype, self.budget, self.n_sink, self.recent, "high", "proj",
+                                 self.filters, self.sign)
+        self.held_k = self.held_v = None
+        self.inner.update(k_all, v_all, scores_in)
+
+    def kept(self, g: int):
+        """(k, v, s, pos) of group g; s is None while rows are only held."""
+        if self.inner is not None:
+            return self.inner.kept(g)
+        n = self.held_k.shape[1]
+        return self.held_k[g], self.held_v[g], None, np.arange(n, dtype=np.int32)

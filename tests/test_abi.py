@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -73,6 +73,19 @@ def test_validation_rejects_bad_calls_without_launching():
                                FAKE, FAKE, FAKE, FAKE, None), -2),
         ("kv_evict_one_inplace", (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, sh, 65, ok, None), -1),
         ("kv_evict_one_inplace", (None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, sh, 64, ok, None), -1),
+        ("kv_passthrough_append", (FAKE, FAKE, 10, 8, FAKE, FAKE, 1, sh, FAKE, FAKE, FAKE, 20, None), -1),
+        ("kv_passthrough_append", (FAKE, FAKE, 5, 8, FAKE, FAKE, 4, sh, FAKE, FAKE, FAKE, 8, None), -1),
+        ("kv_passthrough_append", (None, None, 5, 8, FAKE, FAKE, 1, sh, FAKE, FAKE, FAKE, 8, None), -1),
+        ("kv_passthrough_append", (FAKE, FAKE, 5, 8, FAKE, FAKE, 1, sh, FAKE, FAKE, FAKE, 127, None), -1),  # overlap
+        ("kv_passthrough_append", (None, None, 0, 0, FAKE, FAKE, 8, sh, FAKE, FAKE, FAKE, 8, None), -1),   # new = out
+        ("kv_passthrough_append", (None, None, 0, 0, FAKE, FAKE, 1, api.KvxShape(2, 1, 4, 96, 1),
+                                   FAKE, FAKE, FAKE, 8, None), -1),
+        ("qf_filters_from_keys_device", (FAKE, 1, 4, 1, 8, 128, FAKE, FAKE, 100, None), -1),
+        ("qf_filters_from_keys_device", (FAKE, 1, 4, 16, 8, 128, FAKE, FAKE, 100, None), -1),
+        ("qf_filters_from_keys_device", (FAKE, 1, 4, 16, 16, 128, FAKE, FAKE, 0, None), -1),
+        ("qf_filters_from_keys_device", (FAKE, 1, 4, 16, 16, 256, FAKE, FAKE, 100, None), -2),
+        ("qf_filters_from_keys_device", (FAKE, 7, 4, 16, 16, 128, FAKE, FAKE, 100, None), -1),
+        ("qf_filters_from_keys_device", (FAKE, 1, 4, 16, 16, 128, None, FAKE, 100, None), -1),
     ]
     for fn, args, want in cases:
         rc, msg = _rc(fn, *args)
@@ -81,6 +94,8 @@ def test_validation_rejects_bad_calls_without_launching():
     # zero groups or zero rows: nothing to do, nothing launched
     assert _rc("qf_score_keys", None, api.KvxShape(0, 1, 4, 128, 1), 10, 0, None, 1, None, None)[0] == 0
     assert _rc("kv_evict_topk", None, None, sh, 0, 0, ok, None, None, 0, None)[0] == 0
+    assert _rc("kv_passthrough_append", None, None, 0, 8, None, None, 0, sh, FAKE, FAKE, FAKE, 8, None)[0] == 0
+    assert _rc("qf_filters_from_keys_device", None, 1, 0, 16, 16, 128, None, None, 100, None)[0] == 0
     n = ctypes.c_size_t(99)
     assert _rc("kv_evict_workspace_size", sh, 64, 1, ok, ctypes.byref(n))[0] == 0 and n.value == 0
 

@@ -43,7 +43,7 @@ def _run(cfg, scorer, sample, seed=1234, check_every=None):
     f_lh = synth.filters_mu(cfg) if scorer.filt == "mu" else None
     cache = EvictingCache(cfg.L, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, scorer.mode,
                           None if f_lh is None else torch.from_numpy(f_lh), scorer.sign, cfg.dtype,
-                          calib_tokens=cfg.calib_tokens)
+                          calib_tokens=cfg.calib_tokens, calib_keys=cfg.calib_keys)
     f_s = None
     if f_lh is not None:
         f_s = np.stack([f_lh[cfg.group_lbh(g)[0], cfg.group_lbh(g)[2]] for g in sample])
