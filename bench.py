@@ -14,7 +14,10 @@ projection), c3 (7168 groups, a full cache of budget 2048, then 256
 single-token decode steps with a recent window of 512; the cache is restored
 from a device snapshot, untimed, before each step), c5 (256 groups, 131072
 tokens in 8192-token chunks, budget 8192, key-SVD fallback filters estimated
-before the timed region).
+before the timed region; the estimate's own time is reported beside), qcal (the
+query-SVD calibration of a 28-layer model with 24 query heads over 8 KV heads,
+3000 samples per query head, on the device; a once-per-model step outside the
+eviction path, reported with its own metric).
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
   value        tokens absorbed per second over the whole step (all runs)
@@ -60,7 +63,10 @@ DESCRIPTIONS = {
     "c5": "c5_keysvd_fallback_128k: 32 layers x 8 KV heads x 128 (256 groups), bf16, 131072 tokens in 8192-token "
           "chunks, budget 8192, 4 sinks; projection on key-SVD fallback filters (first 128 keys, estimated "
           "before timing), sign +1",
+    "qcal": "query-SVD calibration: 28 layers x 24 query heads over 8 KV heads x 128, bf16 activations, 3000 "
+            "samples per query head; fp64 Gram + power iteration + GQA averaging per (layer, KV head)",
 }
+PEAK_FP64_TFLOPS = 78.6
 
 
 def log(*a):
@@ -295,6 +301,77 @@ def cpu_baseline(wl, n_groups):
             "sample": "%d of %d groups, every run of the step (%.2f s of oracle time)" % (len(sample), cfg.G, t)}
 
 
+def event_times(torch, stream, fn, n):
+    """Mean milliseconds of fn() over n launches, from HIP events on `stream`."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / n
+
+
+def fallback_estimate_time(torch, wl):
+    """Device time of the key-SVD fallback estimate of the c5 workload (all
+    groups, the first calib_tokens keys of the first chunk)."""
+    from kv_cache_token_amd import api
+    cfg, st = wl.cfg, wl.streams[0]
+    k0 = wl.blocks[0][0]
+    f = torch.empty((cfg.G, D), dtype=torch.float32, device="cuda")
+    status = torch.empty(cfg.G, dtype=torch.int32, device="cuda")
+    fn = lambda: api.qf_filters_from_keys_device(k0, cfg.G, cfg.calib_tokens, k0.shape[1], f, status,  # noqa: E731
+                                                 stream=st)
+    event_times(torch, st, fn, 2)
+    ms = event_times(torch, st, fn, 10)
+    assert int(status.max()) == 0
+    return {"groups": cfg.G, "keys_per_group": cfg.calib_tokens, "mean_us": round(ms * 1e3, 1)}
+
+
+def bench_qcal(torch, args):
+    """The query-SVD calibration at the pages' scale, on the device."""
+    from kv_cache_token_amd import api, synth
+    L, Hq, Hkv, N = 28, 24, 8, 3000
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        q = synth.query_acts_device(L, Hq, Hkv, N, D, seed=1)
+        out = torch.empty((L, Hkv, D), dtype=torch.float32, device="cuda")
+        status = torch.empty((L, Hkv), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    fn = lambda: api.qf_filters_from_queries_device(q, Hkv, out, status, stream=st)  # noqa: E731
+    if args.warmup:
+        event_times(torch, st, fn, args.warmup)
+    ms = event_times(torch, st, fn, args.steps)
+    assert int(status.max()) == 0
+    flops = 2.0 * N * D * D * Hq * L            # the Gram matrices (power iteration not counted)
+    achieved = flops / (ms * 1e-3) / 1e12
+    out_line = {
+        "metric": "query-SVD calibration query heads/sec (fp64 Gram + power iteration + GQA averaging)",
+        "value": round(Hq * L / (ms * 1e-3), 1), "unit": "query heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic (seeded, HBM-resident; rows drift*mu_h + N(0,0.25), heads of a KV group leaning together)",
+        "config": {"workload": DESCRIPTIONS["qcal"], "device": torch.cuda.get_device_name(0)},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP64_TFLOPS, 4), "traffic": None,
+                     "kernel": "top_direction_kernel (Gram flops only)",
+                     "algorithmic_flops_per_launch": int(flops), "mean_launch_us": round(ms * 1e3, 1)},
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle import calib
+        qh = synth.query_acts(1, Hq, Hkv, N, D, seed=1, dtype="bf16")[0]
+        x = synth.bf16_bits_to_f32(qh).astype(np.float64)
+        t0 = time.perf_counter()
+        calib.average_gqa_filters(calib.compute_qfilters(x), Hkv)
+        sec = time.perf_counter() - t0
+        out_line["cpu_baseline"] = {"value": round(Hq / sec, 1), "unit": "query heads/s",
+                                    "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+                                    "kind": "oracle", "sample": "one layer (24 query heads x 3000 x 128), numpy SVD"}
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +396,9 @@ def main():
     from kv_cache_token_amd import _lib
     _lib.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload == "qcal":
+        bench_qcal(torch, args)
+        return
     dev_name = torch.cuda.get_device_name(0)
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
     wl = Workload(torch, args.workload, streams)
@@ -388,6 +468,8 @@ def main():
         "roofline": roof,
         "kernels": breakdown,
     }
+    if args.workload == "c5":
+        out["fallback_estimate"] = fallback_estimate_time(torch, wl)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_groups)
     print(json.dumps(out), flush=True)

@@ -302,6 +302,28 @@ KVX_API int qf_filters_from_keys_device(const void *k, int32_t dtype, int64_t G,
                                         int64_t D, float *out, int32_t *status, int32_t max_iter, void *stream);
 
 /*
+ * qf_filters_from_queries_device -- query-SVD calibration on the device,
+ * batched over layers (Q-Filters page, "Calibrated — the paper's actual
+ * mechanism"): per query head, the top right singular vector v1 of its raw (not
+ * mean-centred) activations Q [N, D], signed by sgn(1^T u1) (the sign of
+ * (column sums of Q) . v1, +1 at zero); the H_q / H_kv filters of the query
+ * heads that share a KV head (contiguous: query head h -> KV head
+ * h / (H_q / H_kv)) are averaged and renormalised.  fp64 Gram matrix and power
+ * iteration, as qf_filters_from_keys_device; one workgroup per (layer, KV head).
+ *   q        device [L, H_q, N, D] of `dtype` (activations of calibration text)
+ *   out      device [L, H_kv, D] float32, unit norm: the filters qf_score_keys reads
+ *   status   device [L, H_kv] int32: 0 ok; 1 a query head's top singular value
+ *            is not separated (or no convergence in max_iter steps); 2 a query
+ *            head's activations are all zero; 3 the group's mean filter is zero
+ * Asynchronous on `stream`; read `status` after synchronising.
+ * Errors: KVX_EINVAL (H_q not a multiple of H_kv, sizes, NULL), KVX_ERANGE
+ * (D = 256; qf_filters_from_queries covers it on the host), KVX_EDEVICE.
+ */
+KVX_API int qf_filters_from_queries_device(const void *q, int32_t dtype, int64_t L, int64_t H_q, int64_t N,
+                                           int64_t D, int64_t H_kv, float *out, int32_t *status, int32_t max_iter,
+                                           void *stream);
+
+/*
  * kvx_stats -- byte accounting of a cache (Q-Filters page, "How it works",
  * last paragraph; L2Norm page, "How it works"): K+V bytes kept and the bytes a
  * full cache of tokens_seen rows would take, their ratio, and the filter bytes

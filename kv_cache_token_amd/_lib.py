@@ -68,6 +68,8 @@ _SIGS = {
     "kv_passthrough_append": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, KvxShape, _vp, _vp, _vp, _i64, _vp],
                               ctypes.c_int),
     "qf_filters_from_keys_device": ([_vp, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _i32, _vp], ctypes.c_int),
+    "qf_filters_from_queries_device": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i32, _vp],
+                                       ctypes.c_int),
     "kvx_stats": ([KvxShape, _i64, _i64, _i32, ctypes.POINTER(KvxStats)], ctypes.c_int),
 }
 

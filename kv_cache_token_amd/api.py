@@ -197,6 +197,19 @@ def qf_filters_from_keys_device(k, G: int, n: int, group_stride: int, out, statu
     return _dispatch("qf_filters_from_keys_device", args, prepare)
 
 
+def qf_filters_from_queries_device(q, H_kv: int, out, status, max_iter: int = 20000, stream=None,
+                                   prepare: bool = False):
+    """Query-SVD calibration on the device: q [L, H_q, N, D] activations ->
+    out [L, H_kv, D] float32 filters, status [L, H_kv] int32."""
+    torch = _torch()
+    code = dtype_code(q.dtype)
+    L, Hq, N, Dd = q.shape
+    args = (_dev(q, "q", torch_dtype(code), L * Hq * N * Dd), code, L, Hq, N, Dd, H_kv,
+            _dev(out, "out", torch.float32, L * H_kv * Dd), _dev(status, "status", torch.int32, L * H_kv),
+            max_iter, _stream(stream))
+    return _dispatch("qf_filters_from_queries_device", args, prepare)
+
+
 # --------------------------------------------------------------------------- host
 
 

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvevict.so")
-SOURCES = ["kvx_device.hip", "kvx_host.cpp"]
+SOURCES = ["kvx_device.hip", "kvx_calib.hip", "kvx_host.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are switched off for all device code.

@@ -15,20 +15,10 @@
 
 #include "kvevict.h"
 #include "kvx_common.h"
+#include "kvx_rows.h"
 
 namespace kvx {
 namespace {
-
-// A K/V row of HD elements of type DT, read 16 bytes per lane.
-template <int DT, int HD>
-struct Row {
-    static constexpr int kElemBytes = DT == KVX_F32 ? 4 : 2;
-    static constexpr int kBytes = HD * kElemBytes;    // e.g. 256 B for a bf16 row of 128
-    static constexpr int kLanes = kBytes / 16;        // lanes covering one row, 16 B each
-    static constexpr int kElemsPerLane = 16 / kElemBytes;
-    static_assert(kLanes >= 1 && kLanes <= 64 && (kLanes & (kLanes - 1)) == 0,
-                  "a row spans a power-of-two number of lanes of one wave");
-};
 
 // Tuning knobs (compile-time): rows in flight per lane and cache hints.
 #ifndef KVX_SCORE_U
@@ -66,51 +56,6 @@ struct Row {
 #ifndef KVX_SELECT_NT
 #define KVX_SELECT_NT 1024
 #endif
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
-
-template <bool NT = false>
-__device__ __forceinline__ uint4 ld16(const char *p) {
-    if constexpr (NT)
-        return to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
-    else
-        return to_uint4(*reinterpret_cast<const u32x4 *>(p));
-}
-template <bool NT = false>
-__device__ __forceinline__ void st16(char *p, uint4 v) {
-    const u32x4 w = {v.x, v.y, v.z, v.w};
-    if constexpr (NT)
-        __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
-    else
-        *reinterpret_cast<u32x4 *>(p) = w;
-}
-
-// Widen the 16 bytes a lane holds to float32 (exact for every element type).
-template <int DT>
-__device__ __forceinline__ void widen(uint4 r, float *x) {
-    if constexpr (DT == KVX_F16) {
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] & 0xFFFFu));
-            x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w[i] >> 16));
-        }
-    } else if constexpr (DT == KVX_BF16) {
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(w[i] << 16);           // element 2i   (low half)
-            x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);  // element 2i+1 (high half)
-        }
-    } else {
-        x[0] = __uint_as_float(r.x);
-        x[1] = __uint_as_float(r.y);
-        x[2] = __uint_as_float(r.z);
-        x[3] = __uint_as_float(r.w);
-    }
-}
 
 // Order-preserving map of a score to an unsigned key, "higher key = better".
 // keep_low ranks by -s.  -0 becomes +0 first so that the two tie.
@@ -814,248 +759,6 @@ __global__ __launch_bounds__(256) void append_rows_kernel(const char *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// Key-SVD fallback filters on the device ("Q-Filters — Query-Agnostic
-// Projection Eviction", "Key-SVD fallback"): per group, the top right singular
-// vector of its first n keys after subtracting their column means, i.e. the
-// top eigenvector of the centred Gram matrix C = Xc^T Xc, signed so that its
-// largest-magnitude entry is positive (lowest index on ties).
-// One workgroup per group, all in fp64: a pass over the keys for the column
-// means, a pass that stages chunks of centred rows in LDS and accumulates C in
-// 8 x 8 register tiles (one per thread), then power iteration on C held in
-// registers until the vector stops moving.
-// ---------------------------------------------------------------------------
-template <int HD>
-struct FbLayout {
-    static constexpr int T = 8;             // Gram tile edge per thread
-    static constexpr int TPR = HD / T;      // threads along one tile row
-    static constexpr int NT = TPR * TPR;    // 64 threads for HD 64, 256 for HD 128
-    static constexpr int CH = 4096 / HD;    // staged rows per chunk (32 KB of fp64)
-    static_assert(NT >= 64 && NT <= 256, "device fallback estimator covers head dims 64 and 128");
-};
-
-__device__ __forceinline__ double shfl_xor_f64(double x, int off) {
-    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
-    const uint32_t lo = __shfl_xor((uint32_t)u, off), hi = __shfl_xor((uint32_t)(u >> 32), off);
-    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-
-template <int DT, int HD>
-__global__ __launch_bounds__(FbLayout<HD>::NT) void fallback_filter_kernel(
-    const char *__restrict__ k, int64_t group_stride, int64_t n, float *__restrict__ out,
-    int32_t *__restrict__ status, int max_iter) {
-    using L = FbLayout<HD>;
-    using R = Row<DT, HD>;
-    constexpr int NT = L::NT, TPR = L::TPR, CH = L::CH, E = R::kElemsPerLane, SLOTS = NT / R::kLanes;
-    static_assert(SLOTS >= 1 && NT % R::kLanes == 0, "a workgroup covers whole rows");
-    __shared__ double xd[CH * HD];  // staged centred rows; first the column partial sums
-    __shared__ double mu[HD], v[HD], y[HD], lam[2];
-    __shared__ int flag;
-    const int t = threadIdx.x, lane = t & 63;
-    const int64_t g = blockIdx.x;
-    const char *kg = k + (size_t)g * group_stride * R::kBytes;
-
-    // column means: thread (slot, part) sums rows slot, slot + SLOTS, ...
-    {
-        const int part = t % R::kLanes, slot = t / R::kLanes;
-        double acc[E];
-#pragma unroll
-        for (int q = 0; q < E; ++q) acc[q] = 0.0;
-        for (int64_t r = slot; r < n; r += SLOTS) {
-            float x[E];
-            widen<DT>(ld16(kg + (size_t)r * R::kBytes + part * 16), x);
-#pragma unroll
-            for (int q = 0; q < E; ++q) acc[q] += (double)x[q];
-        }
-#pragma unroll
-        for (int q = 0; q < E; ++q) xd[slot * HD + part * E + q] = acc[q];
-        __syncthreads();
-        for (int c = t; c < HD; c += NT) {
-            double s = 0.0;
-            for (int j = 0; j < SLOTS; ++j) s += xd[j * HD + c];
-            mu[c] = s / (double)n;
-        }
-        __syncthreads();
-    }
-
-    // centred Gram matrix, tile (r0.., c0..) of 8 x 8 per thread
-    const int tr = t / TPR, tc = t % TPR, r0 = tr * L::T, c0 = tc * L::T;
-    double C[L::T][L::T];
-#pragma unroll
-    for (int i = 0; i < L::T; ++i)
-#pragma unroll
-        for (int j = 0; j < L::T; ++j) C[i][j] = 0.0;
-    for (int64_t base = 0; base < n; base += CH) {
-        const int rows = (int)min((int64_t)CH, n - base);
-        for (int e = t; e < rows * R::kLanes; e += NT) {
-            const int r = e / R::kLanes, part = e % R::kLanes;
-            float x[E];
-            widen<DT>(ld16(kg + (size_t)(base + r) * R::kBytes + part * 16), x);
-#pragma unroll
-            for (int q = 0; q < E; ++q) xd[r * HD + part * E + q] = (double)x[q] - mu[part * E + q];
-        }
-        __syncthreads();
-        for (int r = 0; r < rows; ++r) {
-            double a[L::T], b[L::T];
-#pragma unroll
-            for (int i = 0; i < L::T; ++i) {
-                a[i] = xd[r * HD + r0 + i];
-                b[i] = xd[r * HD + c0 + i];
-            }
-#pragma unroll
-            for (int i = 0; i < L::T; ++i)
-#pragma unroll
-                for (int j = 0; j < L::T; ++j) C[i][j] = __builtin_fma(a[i], b[j], C[i][j]);
-        }
-        __syncthreads();
-    }
-
-    // y = C x over the register tiles (x, y in LDS); ends with a barrier
-    auto matvec = [&](const double *x, double *yv) {
-        double p[L::T];
-#pragma unroll
-        for (int i = 0; i < L::T; ++i) {
-            double s = 0.0;
-#pragma unroll
-            for (int j = 0; j < L::T; ++j) s = __builtin_fma(C[i][j], x[c0 + j], s);
-            p[i] = s;
-        }
-#pragma unroll
-        for (int off = TPR / 2; off > 0; off >>= 1)
-#pragma unroll
-            for (int i = 0; i < L::T; ++i) p[i] += shfl_xor_f64(p[i], off);
-        if (tc == 0)
-#pragma unroll
-            for (int i = 0; i < L::T; ++i) yv[r0 + i] = p[i];
-        __syncthreads();
-    };
-    // wave-0 helpers over HD-long LDS vectors
-    auto wsum = [&](double s) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) s += shfl_xor_f64(s, off);
-        return s;
-    };
-    auto wmax = [&](double s) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) s = fmax(s, shfl_xor_f64(s, off));
-        return s;
-    };
-    // x <- y / |y| (after removing the component along `away` when given);
-    // returns 2 for a zero y, 1 when no entry of x moved by 1e-14, else 0
-    auto renorm = [&](double *x, double *yv, const double *away) {
-        if (away) {
-            double d = 0.0;
-            for (int i = lane; i < HD; i += 64) d += away[i] * yv[i];
-            d = wsum(d);
-            for (int i = lane; i < HD; i += 64) yv[i] -= d * away[i];
-        }
-        double ss = 0.0;
-        for (int i = lane; i < HD; i += 64) ss += yv[i] * yv[i];
-        ss = wsum(ss);
-        const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
-        double dmax = 0.0;
-        for (int i = lane; i < HD; i += 64) {
-            const double nv = yv[i] * inv;
-            dmax = fmax(dmax, fabs(nv - x[i]));
-            x[i] = nv;
-        }
-        dmax = wmax(dmax);
-        return !(ss > 0.0) ? 2 : (dmax < 1e-14 ? 1 : 0);
-    };
-    auto start = [&](double *x, uint32_t salt) {
-        for (int i = t; i < HD; i += NT) {
-            const uint32_t h = ((uint32_t)(i + 1) ^ salt) * 2654435761u;
-            x[i] = ((h >> 31) ? -1.0 : 1.0) * (0.5 + (double)((h >> 8) & 0xFFFF) / 65536.0);
-        }
-    };
-    // power iteration from a fixed, generic start vector; `flag` carries wave
-    // 0's verdict to the workgroup
-    start(v, 0u);
-    __syncthreads();
-    int calm = 0, it = 0, f = 0;
-    for (; it < max_iter; ++it) {
-        matvec(v, y);
-        if (t < 64) {
-            const int r = renorm(v, y, nullptr);
-            if (lane == 0) flag = r;
-        }
-        __syncthreads();
-        f = flag;
-        __syncthreads();  // every thread has read flag before wave 0 rewrites it
-        if (f == 2) break;
-        calm = f == 1 ? calm + 1 : 0;
-        if (calm >= 2) break;
-    }
-    int st = f == 2 ? 2 : (calm >= 2 ? 0 : 1);
-    if (st == 0) {
-        // Separation check: the top eigenvalue must be unique.  lambda1 is the
-        // Rayleigh quotient of v; lambda2 is approached from below by power
-        // iteration restricted to the complement of v (w is kept orthogonal to
-        // v), for at most as many steps again.  Equal top eigenvalues (to 1e-9
-        // relative) are reported like a failure to converge.
-        matvec(v, y);
-        double *w = mu;  // the means are no longer needed
-        if (t < 64) {
-            double l1 = 0.0;
-            for (int i = lane; i < HD; i += 64) l1 += v[i] * y[i];
-            l1 = wsum(l1);
-            if (lane == 0) lam[0] = l1;
-        }
-        start(w, 0x9E3779B9u);
-        __syncthreads();
-        if (t < 64) renorm(w, w, v);  // orthogonalise and normalise the start (w's movement is ignored)
-        __syncthreads();
-        int calm2 = 0;
-        for (int it2 = 0; it2 < it + 64; ++it2) {
-            matvec(w, y);
-            if (t < 64) {
-                double l2 = 0.0;
-                for (int i = lane; i < HD; i += 64) l2 += w[i] * y[i];
-                l2 = wsum(l2);
-                const int r = renorm(w, y, v);
-                if (lane == 0) {
-                    lam[1] = l2;
-                    flag = r;
-                }
-            }
-            __syncthreads();
-            const int f2 = flag;
-            const bool tied = lam[1] >= lam[0] * (1.0 - 1e-9);
-            __syncthreads();
-            if (tied) {
-                st = 1;
-                break;
-            }
-            if (f2 == 2) break;  // nothing outside v: rank one
-            calm2 = f2 == 1 ? calm2 + 1 : 0;
-            if (calm2 >= 2) break;
-        }
-    }
-    if (t < 64) {
-        double best = -1.0;
-        int bi = HD;
-        for (int i = lane; i < HD; i += 64) {
-            const double m = fabs(v[i]);
-            if (m > best) {
-                best = m;
-                bi = i;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const double ob = shfl_xor_f64(best, off);
-            const int oi = __shfl_xor(bi, off);
-            if (ob > best || (ob == best && oi < bi)) {
-                best = ob;
-                bi = oi;
-            }
-        }
-        const double sg = v[bi] > 0.0 ? 1.0 : -1.0;
-        for (int i = lane; i < HD; i += 64) out[(size_t)g * HD + i] = (float)(sg * v[i]);
-        if (lane == 0) status[g] = st;
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Host-side validation shared by the entry points.
 // ---------------------------------------------------------------------------
 int check_shape(const kvx_shape &sh, int64_t *G) {
@@ -1086,32 +789,6 @@ int check_params(const kvx_evict_params &p) {
         return set_error(KVX_ERANGE, "params: budget %lld exceeds KVX_MAX_BUDGET (%d)",
                          (long long)p.budget, KVX_MAX_BUDGET);
     return KVX_OK;
-}
-
-int check_launch(const char *what) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return set_error(KVX_EDEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
-    return KVX_OK;
-}
-
-// Calls f(DT, HD) with compile-time constants for the shape's element type and
-// head dim.  `copy_only` maps fp16 onto bf16 (same row bytes) for kernels that
-// only move rows.
-template <class F>
-int dispatch_row(const kvx_shape &sh, bool copy_only, F &&f) {
-    using bf = std::integral_constant<int, KVX_BF16>;
-    using hf = std::integral_constant<int, KVX_F16>;
-    using fp = std::integral_constant<int, KVX_F32>;
-    auto by_d = [&](auto dt) -> int {
-        switch (sh.D) {
-            case 64: return f(dt, std::integral_constant<int, 64>{});
-            case 128: return f(dt, std::integral_constant<int, 128>{});
-            default: return f(dt, std::integral_constant<int, 256>{});
-        }
-    };
-    if (sh.dtype == KVX_F32) return by_d(fp{});
-    if (sh.dtype == KVX_F16 && !copy_only) return by_d(hf{});
-    return by_d(bf{});
 }
 
 int validate_select_sizes(const kvx_shape &shape, int64_t n_kept, int64_t S, const kvx_evict_params &p,
@@ -1382,33 +1059,6 @@ KVX_API int kv_passthrough_append(const void *k_held, const void *v_held, int64_
         return 0;
     });
     return check_launch("kv_passthrough_append");
-}
-
-KVX_API int qf_filters_from_keys_device(const void *k, int32_t dtype, int64_t G, int64_t n, int64_t group_stride,
-                                        int64_t D, float *out, int32_t *status, int32_t max_iter, void *stream) {
-    clear_error();
-    if (G < 0 || n < 2 || n > KVX_MAX_TOTAL || group_stride < n || max_iter < 1)
-        return set_error(KVX_EINVAL, "qf_filters_from_keys_device: need G >= 0, 2 <= n <= %d, group_stride >= n, "
-                         "max_iter >= 1 (n %lld, group_stride %lld, max_iter %d)", KVX_MAX_TOTAL, (long long)n,
-                         (long long)group_stride, (int)max_iter);
-    if (D != 64 && D != 128)
-        return set_error(KVX_ERANGE, "qf_filters_from_keys_device: head dim %lld (64 or 128 on the device)",
-                         (long long)D);
-    if (dtype != KVX_BF16 && dtype != KVX_F16 && dtype != KVX_F32)
-        return set_error(KVX_EINVAL, "qf_filters_from_keys_device: bad dtype %d", (int)dtype);
-    if (G == 0) return KVX_OK;
-    if (!k || !out || !status) return set_error(KVX_EINVAL, "qf_filters_from_keys_device: NULL buffer");
-    if (G > INT32_MAX) return set_error(KVX_ERANGE, "qf_filters_from_keys_device: too many groups");
-    const kvx_shape sh{1, 1, 1, D, dtype};
-    hipStream_t st = (hipStream_t)stream;
-    dispatch_row(sh, false, [&](auto dt, auto hd) {
-        constexpr int HD = decltype(hd)::value;
-        if constexpr (HD <= 128)
-            fallback_filter_kernel<decltype(dt)::value, HD><<<(uint32_t)G, FbLayout<HD>::NT, 0, st>>>(
-                (const char *)k, group_stride, n, out, status, (int)max_iter);
-        return 0;
-    });
-    return check_launch("qf_filters_from_keys_device");
 }
 
 }  // extern "C"

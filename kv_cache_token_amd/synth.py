@@ -242,6 +242,63 @@ def custom_keys(shape: Tuple[int, ...], seed: int, dtype: str = "bf16", scale: f
 
 
 # ----------------------------------------------------------------------------
+# Query activations for calibration (synthetic stand-in for the pages' 20 x
+# 2048-token calibration text, about 3000 samples per head)
+# ----------------------------------------------------------------------------
+
+def _query_head_dir(l: int, h: int, r: int, D: int, seed: int):
+    """(mu_h, generator for head h's rows) of query_acts."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([5150, seed, l, h // r])))
+    mu = g.standard_normal(D)
+    mu /= np.linalg.norm(mu)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([5151, seed, l, h])))
+    m = mu + 0.25 * rng.standard_normal(D) / np.sqrt(D)
+    return m / np.linalg.norm(m), rng
+
+
+def query_acts(L: int, H_q: int, H_kv: int, N: int, D: int = 128, seed: int = 0, dtype: str = "bf16",
+               workers: int = 16) -> np.ndarray:
+    """[L, H_q, N, D] activations: query head h of layer l (KV head j = h // (H_q/H_kv))
+    has rows drift * mu_h + N(0, 0.5^2), drift ~ U(0.5, 2), with mu_h the unit
+    normalisation of mu_{l,j} + 0.25 xi_h (mu_{l,j} unit, xi_h ~ N(0, I/D)): heads
+    sharing a KV head lean the same way."""
+    from concurrent.futures import ThreadPoolExecutor
+    r = H_q // H_kv
+
+    def one(lh):
+        m, rng = _query_head_dir(lh[0], lh[1], r, D, seed)
+        drift = rng.uniform(0.5, 2.0, (N, 1))
+        return encode((drift * m + 0.5 * rng.standard_normal((N, D))).astype(np.float32), dtype)
+
+    heads = [(l, h) for l in range(L) for h in range(H_q)]
+    with ThreadPoolExecutor(max(1, min(workers, len(heads)))) as ex:
+        rows = list(ex.map(one, heads))
+    return np.stack(rows).reshape(L, H_q, N, D)
+
+
+def query_head_mu(L: int, H_q: int, H_kv: int, D: int = 128, seed: int = 0) -> np.ndarray:
+    """[L, H_q, D] the planted per-head directions mu_h of query_acts."""
+    return np.stack([np.stack([_query_head_dir(l, h, H_q // H_kv, D, seed)[0] for h in range(H_q)])
+                     for l in range(L)])
+
+
+def query_acts_device(L: int, H_q: int, H_kv: int, N: int, D: int = 128, seed: int = 0, device="cuda"):
+    """query_acts' recipe drawn on the device with torch's seeded generator
+    (bf16 [L, H_q, N, D]; not the same bytes as query_acts)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    r = H_q // H_kv
+    mu = torch.randn((L, H_kv, 1, D), generator=gen, device=device)
+    mu = mu / mu.norm(dim=-1, keepdim=True)
+    m = mu.repeat_interleave(r, dim=1) + 0.25 * torch.randn((L, H_q, 1, D), generator=gen, device=device) / D ** 0.5
+    m = m / m.norm(dim=-1, keepdim=True)
+    drift = torch.rand((L, H_q, N, 1), generator=gen, device=device) * 1.5 + 0.5
+    q = torch.randn((L, H_q, N, D), generator=gen, device=device).mul_(0.5).add_(drift * m)
+    return q.to(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------
 # Full-size device inputs (torch is only plumbing here)
 # ----------------------------------------------------------------------------
 

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -86,6 +86,11 @@ def test_validation_rejects_bad_calls_without_launching():
         ("qf_filters_from_keys_device", (FAKE, 1, 4, 16, 16, 256, FAKE, FAKE, 100, None), -2),
         ("qf_filters_from_keys_device", (FAKE, 7, 4, 16, 16, 128, FAKE, FAKE, 100, None), -1),
         ("qf_filters_from_keys_device", (FAKE, 1, 4, 16, 16, 128, None, FAKE, 100, None), -1),
+        ("qf_filters_from_queries_device", (FAKE, 1, 2, 6, 100, 128, 4, FAKE, FAKE, 100, None), -1),  # 6 % 4
+        ("qf_filters_from_queries_device", (FAKE, 1, 2, 6, 0, 128, 2, FAKE, FAKE, 100, None), -1),
+        ("qf_filters_from_queries_device", (FAKE, 1, 2, 6, 100, 256, 2, FAKE, FAKE, 100, None), -2),
+        ("qf_filters_from_queries_device", (FAKE, 1, 2, 6, 100, 128, 2, FAKE, FAKE, 0, None), -1),
+        ("qf_filters_from_queries_device", (None, 1, 2, 6, 100, 128, 2, FAKE, FAKE, 100, None), -1),
     ]
     for fn, args, want in cases:
         rc, msg = _rc(fn, *args)
