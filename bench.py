@@ -257,9 +257,10 @@ def kernel_times(torch, wl, steps):
     return per
 
 
-def cpu_baseline(wl, n_groups):
+def cpu_baseline(wl, n_groups, min_seconds=10.0):
     """The oracle as it stands, on a sample of the same workload (exact seeded
-    host bytes of a sample of groups, every run of the step)."""
+    host bytes of a sample of groups, every run of the step), repeated from the
+    same starting state until at least min_seconds of oracle time have run."""
     import numpy as np
 
     import oracle
@@ -291,14 +292,19 @@ def cpu_baseline(wl, n_groups):
         if cfg.cid == 3:
             oc.update(*pre)               # the decode step starts from a full cache (untimed)
         caches.append(oc)
-    t0 = time.perf_counter()
-    for oc in caches:
-        for K, V in chunks:
-            oc.update(K, V)
-    t = time.perf_counter() - t0
-    tokens = wl.tokens_per_step * len(sample) / cfg.G      # workload-equivalent tokens
+    t, reps = 0.0, 0
+    while reps == 0 or (t < min_seconds and reps < 10000):
+        fresh = [oc.copy() for oc in caches]
+        t0 = time.perf_counter()
+        for oc in fresh:
+            for K, V in chunks:
+                oc.update(K, V)
+        t += time.perf_counter() - t0
+        reps += 1
+    tokens = reps * wl.tokens_per_step * len(sample) / cfg.G      # workload-equivalent tokens
     return {"value": round(tokens / t, 1), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d groups, every run of the step (%.2f s of oracle time)" % (len(sample), cfg.G, t)}
+            "sample": "%d of %d groups, every run of the step, %d repetitions (%.1f s of oracle time)" % (
+                len(sample), cfg.G, reps, t)}
 
 
 def event_times(torch, stream, fn, n):
@@ -381,6 +387,8 @@ def main():
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
                     help="run the step's independent scorer runs on this many streams")
     ap.add_argument("--cpu-groups", type=int, default=32, help="groups in the oracle's timed sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle's sample until this much oracle time has run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as one captured HIP graph (workloads without snapshots, one stream)")
@@ -471,7 +479,7 @@ def main():
     if args.workload == "c5":
         out["fallback_estimate"] = fallback_estimate_time(torch, wl)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_groups)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_groups, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
