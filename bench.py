@@ -49,8 +49,8 @@ KERNEL_SRC = os.path.join(ROOT, "kv_cache_token_amd", "csrc", "kvx_device.hip")
 # copy) summarised in profiles/, valid only for the kernel source they were
 # taken on (sha256 prefix of kvx_device.hip).
 MEASURED_TRAFFIC = {
-    "c4": {"kernel_src_sha256_16": "d943f27a9d8b5118", "bytes_per_launch": 977375790},
-    "c3": {"kernel_src_sha256_16": "d943f27a9d8b5118", "bytes_per_launch": 9141397561},
+    "c4": {"kernel_src_sha256_16": "66f7f41a4c46b656", "bytes_per_launch": 977371432},
+    "c3": {"kernel_src_sha256_16": "66f7f41a4c46b656", "bytes_per_launch": 9128191849},
 }
 DESCRIPTIONS = {
     "c2": "c2_qfilters_calibrated: 28 layers x 8 KV heads x 128 (224 groups), bf16, one 4096-token block, "

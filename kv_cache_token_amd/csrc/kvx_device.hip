@@ -48,10 +48,10 @@ namespace {
 #define KVX_DECODE_NT 1
 #endif
 #ifndef KVX_DECODE_U
-#define KVX_DECODE_U 8
+#define KVX_DECODE_U 12
 #endif
 #ifndef KVX_DECODE_BLOCK
-#define KVX_DECODE_BLOCK 512
+#define KVX_DECODE_BLOCK 1024
 #endif
 #ifndef KVX_SELECT_NT
 #define KVX_SELECT_NT 1024
@@ -582,8 +582,8 @@ __global__ __launch_bounds__(KVX_GATHER_BLOCK) void gather_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode: one incoming row per group, in place.  One 256-thread workgroup per
-// group.  The victim is the candidate with the smallest key, the higher row on
+// Decode: one incoming row per group, in place.  One workgroup per group
+// (KVX_DECODE_BLOCK threads).  The victim is the candidate with the smallest key, the higher row on
 // equal keys (the last row in the general (key desc, row asc) order).  Rows
 // after it move down one row in chunks of C rows: every thread loads its part
 // of the chunk, waits for its loads to land, the workgroup meets at a barrier,
@@ -633,76 +633,91 @@ __global__ __launch_bounds__(KVX_DECODE_BLOCK) void evict_one_kernel(
         best = wbest[0];
 #pragma unroll
         for (int i = 1; i < NB / 64; ++i) best = wbest[i] < best ? wbest[i] : best;
-        const int victim = (int)(0xFFFFFFFFu - (uint32_t)best);
+        const int victim = __builtin_amdgcn_readfirstlane((int)(0xFFFFFFFFu - (uint32_t)best));
         if (victim >= budget) return;  // the incoming row is the one dropped
 
-        const int slot = t % kSlots;
-        const int half = slot / R::kLanes;  // 0: K, 1: V
-        const int part = slot % R::kLanes;
-        const int sub = t / kSlots;
-        char *base = (half ? vc : kc) + part * 16;
+        // The first half of the waves moves K rows, the second half V rows, so
+        // the row base is uniform per wave and lives in a scalar buffer
+        // resource that is rebuilt per chunk; every lane keeps constant offsets.  The
+        // resource of a chunk covers only rows up to budget - 1 of the group:
+        // loads beyond it return zeros and stores beyond it are dropped, so
+        // the body needs no clamping.  Sources past the last row therefore
+        // put zeros on row budget - 1, which the incoming row overwrites.
+        constexpr int kHalfThreads = NB / 2;
+        constexpr int kRowsPerHalfPass = kHalfThreads / R::kLanes;
+        static_assert(kRowsPerHalfPass == kRowsPerPass && kHalfThreads % 64 == 0, "K and V halves of whole waves");
+        const int half = __builtin_amdgcn_readfirstlane(t / kHalfThreads);
+        const int tt = t % kHalfThreads;
+        const int part = tt % R::kLanes;
+        const int sub = tt / R::kLanes;
+        char *base = half ? vc : kc;
+        constexpr int kAux = KVX_DECODE_NT ? 2 : 0;  // slc: the non-temporal hint
+        constexpr int kDw3 = 0x00020000;             // raw buffer, 32-bit data format
         struct Chunk {
-            uint4 d[U];
-            float sv;
-            int32_t pv;
+            u32x4 d[U];
+            uint32_t sv, pv;
         };
-        // Chunk c covers source rows [c0, c0 + C) and is stored one row lower.
-        // The body is branch-free so that the compiler can keep the next
-        // chunk's loads in flight across the wait for this chunk: sources past
-        // the last row read the last row again, and destinations past it land
-        // on row budget - 1, which the incoming row overwrites at the end.
-        const int last = budget - 1;
+        const int lo_off = sub * R::kBytes + part * 16;
+        const int srow = (t % C) * 4;
+        auto rsrc = [&](void *p, int64_t bytes) {
+            return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)(uint32_t)(bytes > 0 ? bytes : 0), kDw3);
+        };
         auto load = [&](Chunk &ch, int c0) {
+            const auto r = rsrc(base + (size_t)c0 * R::kBytes, (int64_t)(budget - c0) * R::kBytes);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int src = min(c0 + u * kRowsPerPass + sub, last);
-                ch.d[u] = ld16<KVX_DECODE_NT>(base + (size_t)src * R::kBytes);
-            }
-            const int sr = min(c0 + (t % C), last);
-            ch.sv = sc[sr];
-            ch.pv = pc[sr];
+            for (int u = 0; u < U; ++u)
+                ch.d[u] = __builtin_amdgcn_raw_buffer_load_b128(r, lo_off + u * kRowsPerPass * R::kBytes, 0, kAux);
+            const auto rs = rsrc(sc + c0, (int64_t)(budget - c0) * 4);
+            const auto rp = rsrc(pc + c0, (int64_t)(budget - c0) * 4);
+            ch.sv = __builtin_amdgcn_raw_buffer_load_b32(rs, srow, 0, 0);
+            ch.pv = __builtin_amdgcn_raw_buffer_load_b32(rp, srow, 0, 0);
         };
-        // Make the compiler wait for this chunk's loads (and only those).
         auto landed = [&](Chunk &ch) {
 #pragma unroll
             for (int u = 0; u < U; ++u) asm volatile("" ::"v"(ch.d[u].x), "v"(ch.d[u].y), "v"(ch.d[u].z), "v"(ch.d[u].w));
             asm volatile("" ::"v"(ch.sv), "v"(ch.pv));
         };
         auto store = [&](const Chunk &ch, int c0) {
+            const auto r = rsrc(base + (size_t)(c0 - 1) * R::kBytes, (int64_t)(budget - c0 + 1) * R::kBytes);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int dst = min(c0 + u * kRowsPerPass + sub - 1, last);
-                st16<KVX_DECODE_NT>(base + (size_t)dst * R::kBytes, ch.d[u]);
-            }
-            if (t < C) {
-                const int dr = min(c0 + t - 1, last);
-                sc[dr] = ch.sv;
-                pc[dr] = ch.pv;
-            }
+            for (int u = 0; u < U; ++u)
+                __builtin_amdgcn_raw_buffer_store_b128(ch.d[u], r, lo_off + u * kRowsPerPass * R::kBytes, 0, kAux);
+            // every thread stores (threads t and t + C hold the same row's values)
+            const auto rs = rsrc(sc + c0 - 1, (int64_t)(budget - c0 + 1) * 4);
+            const auto rp = rsrc(pc + c0 - 1, (int64_t)(budget - c0 + 1) * 4);
+            __builtin_amdgcn_raw_buffer_store_b32(ch.sv, rs, srow, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(ch.pv, rp, srow, 0, 0);
         };
         // Software pipeline: the next chunk's loads are in flight while this
         // chunk waits, meets the barrier and is stored.  The next chunk's
-        // sources lie above every row this chunk writes (except the clamped
-        // last row, whose value is discarded), and every thread has its loads
+        // sources lie above every row this chunk writes (except row budget - 1,
+        // whose value is discarded), and every thread has its loads
         // of this chunk back before the barrier, so no row is overwritten
-        // before it has been read.
+        // before it has been read.  The first chunk is peeled so that every
+        // wait in the loop sees the same operations in flight after its chunk
+        // (the previous chunk's stores and the next chunk's loads) and waits
+        // for its own loads only.
         Chunk a, b;
-        int c0 = victim + 1;
+        const int c0 = victim + 1;
+        int c1 = c0 + C;
         load(a, c0);
-        while (true) {
-            const int c1 = c0 + C;
-            load(b, c1);
-            landed(a);
-            __syncthreads();
-            store(a, c0);
-            if (c1 >= budget) break;
+        load(b, c1);
+        landed(a);
+        __syncthreads();
+        store(a, c0);
+        while (c1 < budget) {
             const int c2 = c1 + C;
             load(a, c2);
             landed(b);
             __syncthreads();
             store(b, c1);
             if (c2 >= budget) break;
-            c0 = c2;
+            const int c3 = c2 + C;
+            load(b, c3);
+            landed(a);
+            __syncthreads();
+            store(a, c2);
+            c1 = c3;
         }
         // Every store (including the discarded ones on row budget - 1) must be
         // complete before the incoming row is written there.
