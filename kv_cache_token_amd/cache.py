@@ -6,6 +6,10 @@ and the true offset (tokens seen, Q-Filters page, "RoPE positions had to be
 fixed first").  Each ``update`` is the query-free step of the pages
 (Q-Filters page and L2Norm page, "How it works"): score the incoming rows,
 select, compact; all arithmetic runs in the library's kernels on one stream.
+A projection cache built without filters runs the key-SVD fallback's lifecycle
+on the device (Q-Filters page, "How it works" step 2, "Key-SVD fallback"):
+rows are held unscored below calib_tokens, and the crossing block freezes one
+filter per group and runs the step over everything held.
 """
 from __future__ import annotations
 
@@ -19,6 +23,17 @@ D = api.D
 
 
 class EvictingCache:
+    """Bounded KV cache of L layers x B sequences x H KV heads (G = L*B*H groups).
+
+    budget, n_sink, recent, keep: the step's parameters (the budget includes the
+    sinks; keep is "low" or "high" for the L2 scorer, always "high" for
+    projection).  mode "l2" or "proj"; filters [L, H, D] float32 for projection,
+    or None with calib_tokens >= 2 for the key-SVD fallback (calib_keys
+    "crossing": estimate from every key held when the crossing block arrives;
+    "first": from the first calib_tokens keys).  dtype "bf16", "f16" or "f32";
+    head_dim 64, 128 or 256.  `stream` is the HIP stream (torch stream or raw
+    handle) every call is enqueued on; None uses torch's current stream."""
+
     def __init__(self, L: int, B: int, H: int, budget: int, n_sink: int = 4, recent: int = 0,
                  keep: str = "low", mode: str = "l2", filters=None, sign: int = 1, dtype: str = "bf16",
                  device="cuda", calib_tokens: int = 0, stream=None, head_dim: int = 128,

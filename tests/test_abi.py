@@ -207,3 +207,19 @@ def test_byte_accounting():
     assert api.kvx_stats(api.make_shape(1, 1, 1, "f16", 64), 10, 5, "l2")["kept_bytes"] == 5 * 2 * 64 * 2
     with pytest.raises(KvxError):
         api.kvx_stats(api.make_shape(1, 1, 1, "f32"), 10, 11, "l2")
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No CPU fallback: without the built library every entry point raises."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from kv_cache_token_amd import _lib, api\n"
+            "_lib.LIB_PATH = %r\n"
+            "try:\n"
+            "    api.kvx_stats(api.make_shape(1, 1, 1, 'bf16'), 1, 1, 'l2')\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n" % (os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                           str(tmp_path / "absent.so")))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert "raised" in out.stdout and "not built" in out.stdout, out.stdout + out.stderr
