@@ -49,8 +49,8 @@ KERNEL_SRC = os.path.join(ROOT, "kv_cache_token_amd", "csrc", "kvx_device.hip")
 # copy) summarised in profiles/, valid only for the kernel source they were
 # taken on (sha256 prefix of kvx_device.hip).
 MEASURED_TRAFFIC = {
-    "c4": {"kernel_src_sha256_16": "66f7f41a4c46b656", "bytes_per_launch": 977371432},
-    "c3": {"kernel_src_sha256_16": "66f7f41a4c46b656", "bytes_per_launch": 9128191849},
+    "c4": {"kernel_src_sha256_16": "53075be3be7412da", "bytes_per_launch": 977371162},
+    "c3": {"kernel_src_sha256_16": "53075be3be7412da", "bytes_per_launch": 9128218185},
 }
 DESCRIPTIONS = {
     "c2": "c2_qfilters_calibrated: 28 layers x 8 KV heads x 128 (224 groups), bf16, one 4096-token block, "
@@ -292,19 +292,73 @@ def cpu_baseline(wl, n_groups, min_seconds=10.0):
         if cfg.cid == 3:
             oc.update(*pre)               # the decode step starts from a full cache (untimed)
         caches.append(oc)
-    t, reps = 0.0, 0
-    while reps == 0 or (t < min_seconds and reps < 10000):
-        fresh = [oc.copy() for oc in caches]
-        t0 = time.perf_counter()
-        for oc in fresh:
-            for K, V in chunks:
-                oc.update(K, V)
-        t += time.perf_counter() - t0
-        reps += 1
-    tokens = reps * wl.tokens_per_step * len(sample) / cfg.G      # workload-equivalent tokens
-    return {"value": round(tokens / t, 1), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+    def run(seconds):
+        t, reps = 0.0, 0
+        while reps == 0 or (t < seconds and reps < 10000):
+            fresh = [oc.copy() for oc in caches]
+            t0 = time.perf_counter()
+            for oc in fresh:
+                for K, V in chunks:
+                    oc.update(K, V)
+            t += time.perf_counter() - t0
+            reps += 1
+        return reps * wl.tokens_per_step * len(sample) / cfg.G / t, reps, t   # workload-equivalent tokens/s
+
+    threads = oracle.num_threads()
+    rate, reps, t = run(min_seconds)
+    oracle.set_num_threads(1)
+    rate1, _, _ = run(min_seconds / 4)
+    oracle.set_num_threads(threads)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(rate, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d groups, every run of the step, %d repetitions (%.1f s of oracle time)" % (
-                len(sample), cfg.G, reps, t)}
+                len(sample), cfg.G, reps, t),
+            "value_1_thread": round(rate1, 1), "cpu_model": model, "host_cpus": os.cpu_count()}
+
+
+def copy_ceiling(torch, stream):
+    """Device-to-device copy rate of the library's own row copy (the
+    passthrough append into a separate buffer): 2 x 256 MiB of bf16 rows read
+    and written, plus 4 B of position per row; GB/s."""
+    from kv_cache_token_amd import api
+    G, S = 1024, 1024
+    shape = api.make_shape(G, 1, 1, "bf16")
+    with torch.cuda.stream(stream):
+        src_k = torch.empty((G, S, D), dtype=torch.bfloat16, device="cuda")
+        src_v = torch.empty_like(src_k)
+        dst_k, dst_v = torch.empty_like(src_k), torch.empty_like(src_k)
+        pos = torch.empty((G, S), dtype=torch.int32, device="cuda")
+    fn = lambda: api.kv_passthrough_append(None, None, 0, 0, src_k, src_v, S, shape, dst_k, dst_v, pos, S,  # noqa: E731
+                                           stream)
+    event_times(torch, stream, fn, 3)
+    ms = event_times(torch, stream, fn, 10)
+    return round((4 * src_k.numel() * 2 + pos.numel() * 4) / (ms * 1e-3) / 1e9, 1)
+
+
+def per_layer_ms(torch, wl, steps):
+    """Secondary number: the same step with one launch sequence per layer (a
+    cache of B x H groups per layer) instead of all layers in each launch."""
+    from kv_cache_token_amd.cache import EvictingCache
+    cfg, st = wl.cfg, wl.streams[0]
+    bh = cfg.B * cfg.H
+    plans = []
+    for sc, whole in zip(cfg.scorers, wl.caches):
+        keep = sc.keep if sc.mode == "l2" else "high"
+        for l in range(cfg.L):
+            f = None if whole.filters is None else whole.filters[l:l + 1]
+            c = EvictingCache(1, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode, f, sc.sign,
+                              cfg.dtype, stream=st)
+            plans.append(c.plan([(k[l * bh:(l + 1) * bh], v[l * bh:(l + 1) * bh]) for k, v in wl.blocks]))
+    run = lambda: [p.run() for p in plans]  # noqa: E731
+    event_times(torch, st, run, 1)
+    return round(event_times(torch, st, run, steps), 4)
 
 
 def event_times(torch, stream, fn, n):
@@ -471,15 +525,22 @@ def main():
         "config": {"workload": DESCRIPTIONS[args.workload], "groups": cfg.G,
                    "tokens_per_step": wl.tokens_per_step, "runs_per_step": len(wl.plans),
                    "budget": cfg.budget, "streams": args.streams, "graph": bool(graph), "device": dev_name},
+        "head_tokens_per_s": round(value * cfg.L * cfg.H, 1),
         "step_algorithmic_GBps": round(step_gbps, 1), "step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
         "step_algorithmic_bytes": int(step_bytes),
+        "device_copy_GBps": copy_ceiling(torch, streams[0]),
         "roofline": roof,
         "kernels": breakdown,
     }
     if args.workload == "c5":
         out["fallback_estimate"] = fallback_estimate_time(torch, wl)
+    if args.workload in ("c2", "c4") and args.streams == 1 and graph is None:
+        out["per_layer_ms_per_step"] = per_layer_ms(torch, wl, max(1, args.steps // 4))
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_groups, args.cpu_seconds)
+        cb = cpu_baseline(wl, args.cpu_groups, args.cpu_seconds)
+        cb["algorithmic_GBps"] = round(cb["value"] * step_bytes / wl.tokens_per_step / 1e9, 2)
+        cb["gpu_speedup"] = round(value / cb["value"], 1)
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

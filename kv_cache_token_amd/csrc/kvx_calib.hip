@@ -1,6 +1,7 @@
-// Filter estimation on the device: the dominant direction of a set of rows,
-// batched over groups, for the two filter sources of "Q-Filters —
-// Query-Agnostic Projection Eviction":
+// The filter side of "Q-Filters — Query-Agnostic Projection Eviction" on the
+// device: the key-SVD fallback's pre-calibration passthrough, and filter
+// estimation (the dominant direction of a set of rows, batched over groups)
+// for the page's two filter sources:
 //
 // * "Key-SVD fallback": the top right singular vector of a group's keys after
 //   subtracting their column means, signed so that its largest-magnitude entry
@@ -34,6 +35,44 @@
 
 namespace kvx {
 namespace {
+
+// ---------------------------------------------------------------------------
+// Pre-calibration passthrough ("Q-Filters — Query-Agnostic Projection
+// Eviction", "How it works" step 2): before the fallback filter exists every
+// row is kept.  out[g, o] = held[g, o] for o < n_held, new[g, o - n_held] after
+// that, positions o (the passthrough only happens from token 0).  When the
+// output is the held buffer itself only the new rows are written (streaming
+// hints: the rows are not read again soon).
+// ---------------------------------------------------------------------------
+template <int DT, int HD>
+__global__ __launch_bounds__(256) void append_rows_kernel(const char *__restrict__ k_held,
+                                                          const char *__restrict__ v_held, int64_t cap_held,
+                                                          int64_t n_held, const char *__restrict__ k_new,
+                                                          const char *__restrict__ v_new, int64_t S, char *k_out,
+                                                          char *v_out, int32_t *pos_out, int64_t cap_out,
+                                                          int64_t first, int64_t G) {
+    using R = Row<DT, HD>;
+    const int64_t rows = n_held + S - first;  // rows written per group
+    const int64_t total = G * rows * R::kLanes;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int part = (int)(e % R::kLanes);
+        const int64_t gr = e / R::kLanes, g = gr / rows, o = first + gr % rows;
+        const char *ks, *vs;
+        if (o < n_held) {
+            ks = k_held + ((size_t)g * cap_held + o) * R::kBytes;
+            vs = v_held + ((size_t)g * cap_held + o) * R::kBytes;
+        } else {
+            ks = k_new + ((size_t)g * S + (o - n_held)) * R::kBytes;
+            vs = v_new + ((size_t)g * S + (o - n_held)) * R::kBytes;
+        }
+        const size_t od = ((size_t)g * cap_out + o) * R::kBytes + part * 16;
+        const uint4 kx = ld16<true>(ks + part * 16), vx = ld16<true>(vs + part * 16);
+        st16<true>(k_out + od, kx);
+        st16<true>(v_out + od, vx);
+        if (part == 0) pos_out[(size_t)g * cap_out + o] = (int32_t)o;
+    }
+}
 
 enum { DIR_CENTRED_KEYS = 0, DIR_RAW_QUERIES = 1 };
 
@@ -376,6 +415,51 @@ int launch_direction(const char *what, const void *x, int32_t dtype, int64_t gro
 using namespace kvx;
 
 extern "C" {
+
+KVX_API int kv_passthrough_append(const void *k_held, const void *v_held, int64_t n_held, int64_t cap_held,
+                                  const void *k_new, const void *v_new, int64_t S, kvx_shape shape, void *k_out,
+                                  void *v_out, int32_t *pos_out, int64_t cap_out, void *stream) {
+    clear_error();
+    int64_t G = 0;
+    int rc = check_shape(shape, &G);
+    if (rc) return rc;
+    if (n_held < 0 || S < 0 || cap_held < 0 || cap_out < 0 || n_held > cap_held || n_held + S > cap_out)
+        return set_error(KVX_EINVAL, "kv_passthrough_append: need 0 <= n_held <= cap_held and n_held + S <= cap_out "
+                         "(n_held %lld, cap_held %lld, S %lld, cap_out %lld)", (long long)n_held, (long long)cap_held,
+                         (long long)S, (long long)cap_out);
+    if (n_held + S > INT32_MAX) return set_error(KVX_ERANGE, "kv_passthrough_append: positions beyond int32");
+    if (G == 0 || n_held + S == 0) return KVX_OK;
+    if (!k_out || !v_out || !pos_out || (S > 0 && (!k_new || !v_new)) || (n_held > 0 && (!k_held || !v_held)))
+        return set_error(KVX_EINVAL, "kv_passthrough_append: NULL buffer");
+    const size_t row = (size_t)shape.D * (shape.dtype == KVX_F32 ? 4 : 2);
+    const bool alias = k_out == k_held && v_out == v_held && cap_out == cap_held;
+    auto overlap = [](const void *a, size_t na, const void *b, size_t nb) {
+        const char *x = (const char *)a, *y = (const char *)b;
+        return a && b && na && nb && x < y + nb && y < x + na;
+    };
+    const size_t out_b = (size_t)G * cap_out * row, held_b = (size_t)G * cap_held * row,
+                 new_b = (size_t)G * S * row;
+    if (!alias && n_held > 0 &&
+        (overlap(k_out, out_b, k_held, held_b) || overlap(k_out, out_b, v_held, held_b) ||
+         overlap(v_out, out_b, k_held, held_b) || overlap(v_out, out_b, v_held, held_b)))
+        return set_error(KVX_EINVAL, "kv_passthrough_append: output overlaps the held rows without being them");
+    if (overlap(k_out, out_b, k_new, new_b) || overlap(k_out, out_b, v_new, new_b) ||
+        overlap(v_out, out_b, k_new, new_b) || overlap(v_out, out_b, v_new, new_b) ||
+        overlap(k_out, out_b, v_out, out_b))
+        return set_error(KVX_EINVAL, "kv_passthrough_append: output overlaps the new rows or itself");
+    const int64_t first = alias ? n_held : 0;
+    const int64_t lanes = G * (n_held + S - first) * (int64_t)(row / 16);
+    if (lanes == 0) return KVX_OK;
+    const uint32_t grid = (uint32_t)std::min<int64_t>((lanes + 255) / 256, 65536);
+    hipStream_t st = (hipStream_t)stream;
+    dispatch_row(shape, true, [&](auto dt, auto hd) {
+        append_rows_kernel<decltype(dt)::value, decltype(hd)::value><<<grid, 256, 0, st>>>(
+            (const char *)k_held, (const char *)v_held, cap_held, n_held, (const char *)k_new, (const char *)v_new,
+            S, (char *)k_out, (char *)v_out, pos_out, cap_out, first, G);
+        return 0;
+    });
+    return check_launch("kv_passthrough_append");
+}
 
 KVX_API int qf_filters_from_keys_device(const void *k, int32_t dtype, int64_t G, int64_t n, int64_t group_stride,
                                         int64_t D, float *out, int32_t *status, int32_t max_iter, void *stream) {

@@ -69,6 +69,22 @@ __device__ __forceinline__ void widen(uint4 r, float *x) {
     }
 }
 
+// Validates a shape (sizes, head dim, element type) and returns its group count.
+inline int check_shape(const kvx_shape &sh, int64_t *G) {
+    if (sh.L < 0 || sh.B < 0 || sh.H < 0)
+        return set_error(KVX_EINVAL, "shape: L, B, H must be >= 0 (got %lld, %lld, %lld)",
+                         (long long)sh.L, (long long)sh.B, (long long)sh.H);
+    if (sh.D != 64 && sh.D != 128 && sh.D != 256)
+        return set_error(KVX_EINVAL, "shape: D must be 64, 128 or 256 (got %lld)", (long long)sh.D);
+    if (sh.dtype != KVX_BF16 && sh.dtype != KVX_F32 && sh.dtype != KVX_F16)
+        return set_error(KVX_EINVAL, "shape: dtype must be KVX_BF16, KVX_F16 or KVX_F32 (got %d)", (int)sh.dtype);
+    if (sh.L > INT32_MAX || sh.B > INT32_MAX || sh.H > INT32_MAX ||
+        (sh.L > 0 && sh.B > 0 && sh.H > 0 && sh.L * sh.B > INT32_MAX / sh.H))
+        return set_error(KVX_ERANGE, "shape: L*B*H must be below 2^31");
+    *G = sh.L * sh.B * sh.H;
+    return KVX_OK;
+}
+
 // Launch status of the last kernel on this thread, as a library status.
 inline int check_launch(const char *what) {
     const hipError_t e = hipGetLastError();

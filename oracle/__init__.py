@@ -60,7 +60,8 @@ def lib():
         L.orc_groups_update.argtypes = [i64, i64, i64, i32, i32, vp, i32, i64, i64, i64, i32,
                                         vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
         L.orc_num_threads.argtypes = []
-        for f in (L.orc_score, L.orc_select, L.orc_groups_update, L.orc_num_threads):
+        L.orc_set_num_threads.argtypes = [i32]
+        for f in (L.orc_score, L.orc_select, L.orc_groups_update, L.orc_num_threads, L.orc_set_num_threads):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -91,6 +92,11 @@ def _dt(x: np.ndarray, dtype: Optional[str] = None) -> int:
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops over groups (timing baselines)."""
+    _check(lib().orc_set_num_threads(n), "orc_set_num_threads")
 
 
 def score(k: np.ndarray, mode: str = "l2", f: Optional[np.ndarray] = None, sign: int = 1,

@@ -312,3 +312,16 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads the next parallel loops use (timing baselines only). */
+int orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n < 1) return -1;
+    omp_set_num_threads(n);
+    return 0;
+#else
+    return n == 1 ? 0 : -1;
+#endif
+}
