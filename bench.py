@@ -74,9 +74,11 @@ def log(*a):
 
 
 class Workload:
-    """One plan per scorer run over HBM-resident seeded inputs."""
+    """One plan per scorer run over HBM-resident seeded inputs; with split > 1
+    each run's groups are divided by layer into that many independent caches
+    (the step is per group), spread over the streams."""
 
-    def __init__(self, torch, name, streams):
+    def __init__(self, torch, name, streams, split=1):
         from kv_cache_token_amd import synth
         from kv_cache_token_amd.cache import EvictingCache
         cid = int(name[1:])
@@ -92,24 +94,37 @@ class Workload:
             else:
                 self.blocks = [synth.fill_device(cfg, S, 1000 * cid + c, mus=mus) for c, S in enumerate(cfg.chunks)]
             f_mu = torch.from_numpy(synth.filters_mu(cfg)).cuda() if cfg.keys == "aniso" else None
-        self.caches, self.plans, self.snapshots = [], [], []
+        self.f_mu = f_mu
+        if split < 1 or cfg.L % split:
+            raise ValueError("split must divide the layer count %d" % cfg.L)
+        per = cfg.L // split
+        bh = cfg.B * cfg.H
+
+        def part(blocks, l0, l1):
+            return [(k[l0 * bh:l1 * bh], v[l0 * bh:l1 * bh]) for k, v in blocks]
+
+        self.caches, self.plans, self.snapshots, self.ranges = [], [], [], []
         for i, sc in enumerate(cfg.scorers):
-            st = streams[i % len(streams)]
             keep = sc.keep if sc.mode == "l2" else "high"
-            c = EvictingCache(cfg.L, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode,
-                              f_mu if sc.filt == "mu" else None, sc.sign, cfg.dtype, stream=st,
-                              calib_tokens=cfg.calib_tokens, calib_keys=cfg.calib_keys)
-            with torch.cuda.stream(st):
-                if sc.filt == "keysvd":       # freeze the fallback filters once, outside the timed step
-                    c.update(*self.blocks[0])
-                    c.reset(keep_filters=True)
-                if cid == 3:                  # the decode step starts from a full cache
-                    c.update(*prefill)
-                    self.snapshots.append([x.clone() for x in c.buffers()])
-                    self.plans.append(c.plan(self.blocks, keep_state=True))
-                else:
-                    self.plans.append(c.plan(self.blocks))
-            self.caches.append(c)
+            for p in range(split):
+                l0, l1 = p * per, (p + 1) * per
+                st = streams[(i * split + p) % len(streams)]
+                c = EvictingCache(per, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode,
+                                  f_mu[l0:l1] if sc.filt == "mu" else None, sc.sign, cfg.dtype, stream=st,
+                                  calib_tokens=cfg.calib_tokens, calib_keys=cfg.calib_keys)
+                blocks = part(self.blocks, l0, l1)
+                with torch.cuda.stream(st):
+                    if sc.filt == "keysvd":       # freeze the fallback filters once, outside the timed step
+                        c.update(*blocks[0])
+                        c.reset(keep_filters=True)
+                    if cid == 3:                  # the decode step starts from a full cache
+                        c.update(*part([prefill], l0, l1)[0])
+                        self.snapshots.append([x.clone() for x in c.buffers()])
+                        self.plans.append(c.plan(blocks, keep_state=True))
+                    else:
+                        self.plans.append(c.plan(blocks))
+                self.caches.append(c)
+                self.ranges.append((l0, l1))
         # Inputs that fit a few times in the 256 MB last-level cache (c2) are
         # rotated between two seeded sets, so that a step never re-reads the
         # previous step's inputs from that cache.
@@ -118,7 +133,7 @@ class Workload:
         if in_bytes < (1 << 30) and not self.snapshots and all(sc.filt != "keysvd" for sc in cfg.scorers):
             with torch.cuda.stream(streams[0]):
                 alt = [synth.fill_device(cfg, S, 1000 * cid + 500 + c, mus=mus) for c, S in enumerate(cfg.chunks)]
-            self.plan_sets.append([c.plan(alt) for c in self.caches])
+            self.plan_sets.append([c.plan(part(alt, l0, l1)) for c, (l0, l1) in zip(self.caches, self.ranges)])
         self._turn = 0
         torch.cuda.synchronize()
         self.tokens_per_step = len(cfg.scorers) * cfg.B * sum(b[0].shape[1] for b in self.blocks)
@@ -362,10 +377,10 @@ def per_layer_ms(torch, wl, steps):
     cfg, st = wl.cfg, wl.streams[0]
     bh = cfg.B * cfg.H
     plans = []
-    for sc, whole in zip(cfg.scorers, wl.caches):
+    for sc in cfg.scorers:
         keep = sc.keep if sc.mode == "l2" else "high"
         for l in range(cfg.L):
-            f = None if whole.filters is None else whole.filters[l:l + 1]
+            f = wl.f_mu[l:l + 1] if sc.filt == "mu" else None
             c = EvictingCache(1, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode, f, sc.sign,
                               cfg.dtype, stream=st)
             plans.append(c.plan([(k[l * bh:(l + 1) * bh], v[l * bh:(l + 1) * bh]) for k, v in wl.blocks]))
@@ -451,8 +466,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
-                    help="run the step's independent scorer runs on this many streams")
+    ap.add_argument("--streams", type=int, default=1, choices=(1, 2, 4),
+                    help="streams the step's independent caches are spread over")
+    ap.add_argument("--split", type=int, default=1,
+                    help="divide each run's groups by layer into this many independent caches")
     ap.add_argument("--cpu-groups", type=int, default=32, help="groups in the oracle's timed sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle's sample until this much oracle time has run")
@@ -476,7 +493,7 @@ def main():
         return
     dev_name = torch.cuda.get_device_name(0)
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
-    wl = Workload(torch, args.workload, streams)
+    wl = Workload(torch, args.workload, streams, args.split)
     cfg = wl.cfg
     log("workload %s ready on %s: %d groups, %d calls per run" % (args.workload, dev_name, cfg.G, len(wl.blocks)))
 
@@ -537,7 +554,7 @@ def main():
             "aniso": "drift*mu + N(0,0.25)", "lognorm": "r*u, ln r ~ N(0,0.25)", "gauss": "N(0,1)"}[cfg.keys],
         "config": {"workload": DESCRIPTIONS[args.workload], "groups": cfg.G,
                    "tokens_per_step": wl.tokens_per_step, "runs_per_step": len(wl.plans),
-                   "budget": cfg.budget, "streams": args.streams, "graph": bool(graph),
+                   "budget": cfg.budget, "streams": args.streams, "split": args.split, "graph": bool(graph),
                    "input_sets": len(wl.plan_sets), "device": dev_name},
         "head_tokens_per_s": round(value * cfg.L * cfg.H, 1),
         "step_algorithmic_GBps": round(step_gbps, 1), "step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
@@ -548,7 +565,7 @@ def main():
     }
     if args.workload == "c5":
         out["fallback_estimate"] = fallback_estimate_time(torch, wl)
-    if args.workload in ("c2", "c4") and args.streams == 1 and graph is None:
+    if args.workload in ("c2", "c4") and args.streams == 1 and args.split == 1 and graph is None:
         out["per_layer_ms_per_step"] = per_layer_ms(torch, wl, max(1, args.steps // 4))
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wl, args.cpu_groups, args.cpu_seconds)
