@@ -14,15 +14,18 @@
 //   attention the filters of the query heads sharing a KV head are averaged
 //   and renormalised.
 //
-// Both are the top eigenvector of a Gram matrix C = X^T X (X centred or raw).
-// One workgroup per group: a pass over the rows for the fp64 column sums, a
-// pass that stages chunks of rows (centred when asked) in LDS as fp64 and
-// accumulates C in 8 x 8 fp64 register tiles, then power iteration with C held
-// in registers, and a bounded second iteration on the complement of the found
-// vector that checks that the top eigenvalue is separated.  When the iteration
-// is slow (top two eigenvalues close), C is squared in place every 32 steps (up
-// to 2^10-th powers, rescaled by a power of two): the eigenvectors stay, the
-// ratio of the top two eigenvalues is squared.
+// Both are the top eigenvector of a Gram matrix C = X^T X (X centred or raw),
+// a dense fp64 contraction, done on the matrix cores (v_mfma_f64_16x16x4f64).
+// One workgroup per group, one wave per 64 x 64 quadrant of C held as 16
+// accumulator tiles of 16 x 16: a pass over the rows for the fp64 column sums,
+// a pass that stages chunks of rows (centred when asked) in LDS as fp64 and
+// feeds them four rows at a time to the tiles, then power iteration with C
+// held in the tiles, and a bounded second iteration on the complement of the
+// found vector that checks that the top eigenvalue is separated.  When the
+// iteration is slow (top two eigenvalues close), C is squared in place every 32
+// steps (C staged in LDS, the product again on the matrix cores; up to 2^10-th
+// powers, rescaled by a power of two): the eigenvectors stay, the ratio of the
+// top two eigenvalues is squared.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,14 +81,22 @@ enum { DIR_CENTRED_KEYS = 0, DIR_RAW_QUERIES = 1 };
 
 template <int HD>
 struct DirLayout {
-    static constexpr int T = 8;            // Gram tile edge per thread
-    static constexpr int TPR = HD / T;     // threads along one tile row
-    static constexpr int NT = TPR * TPR;   // 64 threads for HD 64, 256 for HD 128
+    static constexpr int QW = HD / 64;     // quadrants of C per side
+    static constexpr int NT = 64 * QW * QW;  // one wave per quadrant: 64 threads for HD 64, 256 for HD 128
     static constexpr int CH = HD;          // staged rows per chunk: an HD x HD fp64 square of LDS
+    static constexpr int S = HD + 1;       // LDS row stride in doubles (column reads hit distinct banks)
     static constexpr int SQUARE_EVERY = 32;  // power steps between squarings of C
     static constexpr int MAX_SQUARINGS = 10;
-    static_assert(NT >= 64 && NT <= 256, "the device estimator covers head dims 64 and 128");
+    static_assert(QW == 1 || QW == 2, "the device estimator covers head dims 64 and 128");
 };
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// One 16 x 16 x 4 fp64 matrix-core product: lane l gives A[l % 16][l / 16] and
+// B[l / 16][l % 16]; element q of the result holds D[l / 16 + 4q][l % 16].
+__device__ __forceinline__ f64x4 mfma16x16x4(double a, double b, f64x4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ double shfl_xor_f64(double x, int off) {
     const unsigned long long u = (unsigned long long)__double_as_longlong(x);
@@ -105,35 +116,56 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
     int32_t *__restrict__ status, int max_iter) {
     using L = DirLayout<HD>;
     using R = Row<DT, HD>;
-    constexpr int NT = L::NT, TPR = L::TPR, CH = L::CH, E = R::kElemsPerLane, SLOTS = NT / R::kLanes;
+    constexpr int NT = L::NT, CH = L::CH, S = L::S, E = R::kElemsPerLane, SLOTS = NT / R::kLanes;
     static_assert(SLOTS >= 1 && NT % R::kLanes == 0, "a workgroup covers whole rows");
     static_assert(SLOTS <= CH, "the column partial sums fit the staging buffer");
-    __shared__ double xd[CH * HD];  // staged rows, or C while it is squared; first the column partial sums
-    __shared__ double cs[HD], v[HD], y[HD], w[HD], acc[HD], lam[2], red[NT / 64];
+    __shared__ double xd[CH * S];  // staged rows, or C while it is squared; first the column partial sums
+    __shared__ double cs[HD], mu[HD], v[HD], y[HD], w[HD], acc[HD], yp[L::QW][HD], lam[2], red[NT / 64];
     __shared__ int flag;
-    const int t = threadIdx.x, lane = t & 63;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int lr = lane & 15, lk = lane >> 4;
+    const int R0 = (wv / L::QW) * 64, C0 = (wv % L::QW) * 64;  // this wave's quadrant of C
     const int64_t g = blockIdx.x;
-    const int tr = t / TPR, tc = t % TPR, r0 = tr * L::T, c0 = tc * L::T;
 
-    // y = C x over the register tiles (x, y in LDS); ends with a barrier
-    double C[L::T][L::T];
-    auto matvec = [&](const double *xv, double *yv) {
-        double p[L::T];
+    // C[R0 + 16a + lk + 4q][C0 + 16b + lr] = Cm[a][b][q]
+    f64x4 Cm[4][4];
+    auto zero_c = [&]() {
 #pragma unroll
-        for (int i = 0; i < L::T; ++i) {
-            double s = 0.0;
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int j = 0; j < L::T; ++j) s = __builtin_fma(C[i][j], xv[c0 + j], s);
-            p[i] = s;
+            for (int b = 0; b < 4; ++b) Cm[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    };
+    // y = C x, as C^T x (C is symmetric): each lane sums its 16 entries of a
+    // column, the four lanes of a column meet by two shuffles, and each
+    // quadrant's column sums go to yp (ends with a barrier); wave 0 then adds
+    // the quadrants of a column band (gather_y)
+    auto matvec = [&](const double *xv) {
+        double p[4] = {0.0, 0.0, 0.0, 0.0};  // p[b]: part of y[C0 + 16b + lr]
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double xi = xv[R0 + 16 * a + lk + 4 * q];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) p[b] = __builtin_fma(Cm[a][b][q], xi, p[b]);
+            }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            p[b] += shfl_xor_f64(p[b], 16);
+            p[b] += shfl_xor_f64(p[b], 32);
         }
+        if (lk == 0)
 #pragma unroll
-        for (int off = TPR / 2; off > 0; off >>= 1)
-#pragma unroll
-            for (int i = 0; i < L::T; ++i) p[i] += shfl_xor_f64(p[i], off);
-        if (tc == 0)
-#pragma unroll
-            for (int i = 0; i < L::T; ++i) yv[r0 + i] = p[i];
+            for (int b = 0; b < 4; ++b) yp[wv / L::QW][C0 + 16 * b + lr] = p[b];
         __syncthreads();
+    };
+    auto gather_y = [&]() {  // wave 0
+        for (int i = lane; i < HD; i += 64) {
+            double s = yp[0][i];
+#pragma unroll
+            for (int h = 1; h < L::QW; ++h) s += yp[h][i];
+            y[i] = s;
+        }
     };
     // wave-0 reductions and vector updates over HD-long LDS vectors
     auto wsum = [&](double s) {
@@ -170,31 +202,31 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
     auto square = [&]() {
         __syncthreads();  // nobody reads xd any more
 #pragma unroll
-        for (int i = 0; i < L::T; ++i)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int j = 0; j < L::T; ++j) xd[(r0 + i) * HD + c0 + j] = C[i][j];
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xd[(R0 + 16 * a + lk + 4 * q) * S + C0 + 16 * b + lr] = Cm[a][b][q];
         __syncthreads();
+        zero_c();
+        for (int k0 = 0; k0 < HD; k0 += 4) {
+            double av[4], bv[4];
 #pragma unroll
-        for (int i = 0; i < L::T; ++i)
+            for (int a = 0; a < 4; ++a) av[a] = xd[(R0 + 16 * a + lr) * S + k0 + lk];  // A[i][k] = C[i][k]
 #pragma unroll
-            for (int j = 0; j < L::T; ++j) C[i][j] = 0.0;
-        for (int k = 0; k < HD; ++k) {
-            double a[L::T], b[L::T];
+            for (int b = 0; b < 4; ++b) bv[b] = xd[(k0 + lk) * S + C0 + 16 * b + lr];  // B[k][j] = C[k][j]
 #pragma unroll
-            for (int i = 0; i < L::T; ++i) {
-                a[i] = xd[k * HD + r0 + i];
-                b[i] = xd[k * HD + c0 + i];
-            }
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int i = 0; i < L::T; ++i)
-#pragma unroll
-                for (int j = 0; j < L::T; ++j) C[i][j] = __builtin_fma(a[i], b[j], C[i][j]);
+                for (int b = 0; b < 4; ++b) Cm[a][b] = mfma16x16x4(av[a], bv[b], Cm[a][b]);
         }
         double m = 0.0;
 #pragma unroll
-        for (int i = 0; i < L::T; ++i)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int j = 0; j < L::T; ++j) m = fmax(m, fabs(C[i][j]));
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) m = fmax(m, fabs(Cm[a][b][q]));
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) m = fmax(m, shfl_xor_f64(m, off));
         if (lane == 0) red[t / 64] = m;
@@ -203,9 +235,9 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
         for (int i = 0; i < NT / 64; ++i) mx = fmax(mx, red[i]);
         const double scale = mx > 0.0 ? ldexp(1.0, -ilogb(mx)) : 1.0;
 #pragma unroll
-        for (int i = 0; i < L::T; ++i)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int j = 0; j < L::T; ++j) C[i][j] *= scale;
+            for (int b = 0; b < 4; ++b) Cm[a][b] *= scale;
         __syncthreads();  // red and xd are free again
     };
     // a fixed, generic start vector
@@ -220,77 +252,120 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
     int worst = 0;
     for (int q = 0; q < r; ++q) {
         const char *xg = x + (size_t)(g * r + q) * stride * R::kBytes;
-        // column sums: thread (slot, part) sums rows slot, slot + SLOTS, ...
-        {
-            const int part = t % R::kLanes, slot = t / R::kLanes;
-            double a[E];
+        // Column sums (their mean centres the keys; their dot with v signs a
+        // query filter).  Thread (slot, part) always covers the same 16-byte
+        // column slice `part`; its rows are summed in registers and the slots
+        // meet in LDS.  Centred keys need the means before the Gram pass, so
+        // they take a pass of their own; raw queries sum while staging.
+        constexpr int kPer = CH * R::kLanes / NT;  // staged loads per thread per chunk
+        const int part = t % R::kLanes, slot = t / R::kLanes;
+        double csum[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) a[e] = 0.0;
-            for (int64_t row = slot; row < n; row += SLOTS) {
-                float f[E];
-                widen<DT>(ld16(xg + (size_t)row * R::kBytes + part * 16), f);
+        for (int e = 0; e < E; ++e) csum[e] = 0.0;
+        auto reduce_sums = [&]() {
+            __syncthreads();  // xd is free
 #pragma unroll
-                for (int e = 0; e < E; ++e) a[e] += (double)f[e];
-            }
-            __syncthreads();  // the previous head is done with xd
-#pragma unroll
-            for (int e = 0; e < E; ++e) xd[slot * HD + part * E + e] = a[e];
+            for (int e = 0; e < E; ++e) xd[slot * HD + part * E + e] = csum[e];
             __syncthreads();
             for (int c = t; c < HD; c += NT) {
                 double s = 0.0;
                 for (int j = 0; j < SLOTS; ++j) s += xd[j * HD + c];
                 cs[c] = s;
+                mu[c] = s / (double)n;  // a division, so that n equal rows centre to exact zeros
             }
             __syncthreads();
+        };
+        if constexpr (MODE == DIR_CENTRED_KEYS) {
+            // kLoads rows in flight per thread; rows past n read row n - 1 and add nothing
+            constexpr int kLoads = 8;
+            for (int64_t row0 = slot; row0 < n; row0 += (int64_t)SLOTS * kLoads) {
+                uint4 raw[kLoads];
+#pragma unroll
+                for (int u = 0; u < kLoads; ++u) {
+                    const int64_t row = min(row0 + (int64_t)u * SLOTS, n - 1);
+                    raw[u] = ld16(xg + (size_t)row * R::kBytes + part * 16);
+                }
+#pragma unroll
+                for (int u = 0; u < kLoads; ++u) {
+                    if (row0 + (int64_t)u * SLOTS >= n) break;
+                    float f[E];
+                    widen<DT>(raw[u], f);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) csum[e] += (double)f[e];
+                }
+            }
+            reduce_sums();
         }
-        // Gram matrix of the (centred) rows, tile (r0.., c0..) of 8 x 8 per thread
+        // Gram matrix of the (centred) rows: A = X^T and B = X, four rows a
+        // step.  The loads of chunk c + 1 are in flight while chunk c is on the
+        // matrix cores; rows past a chunk read its last row and are not used.
+        zero_c();
+        uint4 raw[kPer];
+        auto fetch = [&](int64_t base) {
+            const int rows = (int)min((int64_t)CH, n - base);
 #pragma unroll
-        for (int i = 0; i < L::T; ++i)
-#pragma unroll
-            for (int j = 0; j < L::T; ++j) C[i][j] = 0.0;
-        const double inv_n = 1.0 / (double)n;
+            for (int u = 0; u < kPer; ++u) {
+                const int rr = min((t + u * NT) / R::kLanes, rows - 1);
+                raw[u] = ld16(xg + (size_t)(base + rr) * R::kBytes + part * 16);
+            }
+        };
+        fetch(0);
         for (int64_t base = 0; base < n; base += CH) {
             const int rows = (int)min((int64_t)CH, n - base);
-            for (int e = t; e < rows * R::kLanes; e += NT) {
-                const int rr = e / R::kLanes, part = e % R::kLanes;
+            __syncthreads();  // the previous chunk's products have read xd
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const int rr = (t + u * NT) / R::kLanes;
+                if (rr >= rows) break;
                 float f[E];
-                widen<DT>(ld16(xg + (size_t)(base + rr) * R::kBytes + part * 16), f);
+                widen<DT>(raw[u], f);
 #pragma unroll
                 for (int k = 0; k < E; ++k) {
                     const int c = part * E + k;
-                    xd[rr * HD + c] = MODE == DIR_CENTRED_KEYS ? (double)f[k] - cs[c] * inv_n : (double)f[k];
+                    if constexpr (MODE == DIR_CENTRED_KEYS) {
+                        xd[rr * S + c] = (double)f[k] - mu[c];
+                    } else {
+                        xd[rr * S + c] = (double)f[k];
+                        csum[k] += (double)f[k];
+                    }
                 }
             }
+            if (base + CH < n) fetch(base + CH);
             __syncthreads();
-            for (int rr = 0; rr < rows; ++rr) {
-                double a[L::T], b[L::T];
+            for (int k0 = 0; k0 < rows; k0 += 4) {
+                // rows past the chunk's end count as zeros (k < CH since CH % 4 == 0)
+                const int k = k0 + lk;
+                const bool in = k < rows;
+                double av[4], bv[4];
 #pragma unroll
-                for (int i = 0; i < L::T; ++i) {
-                    a[i] = xd[rr * HD + r0 + i];
-                    b[i] = xd[rr * HD + c0 + i];
-                }
+                for (int a = 0; a < 4; ++a) av[a] = in ? xd[k * S + R0 + 16 * a + lr] : 0.0;
 #pragma unroll
-                for (int i = 0; i < L::T; ++i)
+                for (int b = 0; b < 4; ++b) bv[b] = in ? xd[k * S + C0 + 16 * b + lr] : 0.0;
 #pragma unroll
-                    for (int j = 0; j < L::T; ++j) C[i][j] = __builtin_fma(a[i], b[j], C[i][j]);
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) Cm[a][b] = mfma16x16x4(av[a], bv[b], Cm[a][b]);
             }
-            __syncthreads();
         }
+        if constexpr (MODE == DIR_RAW_QUERIES) reduce_sums();  // begins with a barrier
+        __syncthreads();
 
         // power iteration; `flag` carries wave 0's verdict to the workgroup
         start(v, 0u);
         __syncthreads();
         int calm = 0, it = 0, f = 0, squarings = 0;
         double power = 1.0;  // C now holds the original C to this power
+        // (flag and lam are rewritten by wave 0 only after the next mat-vec's
+        // barrier, which every thread reaches after reading them)
         for (; it < max_iter; ++it) {
-            matvec(v, y);
+            matvec(v);
             if (t < 64) {
+                gather_y();
                 const int rc = renorm(v, y, nullptr);
                 if (lane == 0) flag = rc;
             }
             __syncthreads();
             f = flag;
-            __syncthreads();  // every thread has read flag before wave 0 rewrites it
             if (f == 2) break;
             calm = f == 1 ? calm + 1 : 0;
             if (calm >= 2) break;
@@ -305,11 +380,15 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
         if (st == 0) {
             // Separation check: lambda1 is the Rayleigh quotient of v; lambda2 is
             // approached from below by power iteration on the complement of v
-            // (w kept orthogonal to v), for at most as many steps again.  Equal
-            // top eigenvalues (lambda2 >= lambda1 (1 - 1e-9)) are reported as
-            // status 1; on the p-th power of C that is a ratio of 1 - p 1e-9.
-            matvec(v, y);
+            // (w kept orthogonal to v), for at most kSepSteps steps.  Equal top
+            // eigenvalues (lambda2 >= lambda1 (1 - 1e-9)) are reported as status
+            // 1; on the p-th power of C that is a ratio of 1 - p 1e-9.  A tie
+            // whose eigenvalues stand clear of the rest shows within a few steps;
+            // top eigenvalues that are close but not tied have already kept the
+            // main iteration from converging.
+            matvec(v);
             if (t < 64) {
+                gather_y();
                 const double l1 = wdot(v, y);
                 if (lane == 0) lam[0] = l1;
             }
@@ -318,9 +397,11 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
             if (t < 64) renorm(w, w, v);  // orthogonalise and normalise the start
             __syncthreads();
             int calm2 = 0;
-            for (int it2 = 0; it2 < it + 64; ++it2) {
-                matvec(w, y);
+            constexpr int kSepSteps = 48;
+            for (int it2 = 0; it2 < kSepSteps; ++it2) {
+                matvec(w);
                 if (t < 64) {
+                    gather_y();
                     const double l2 = wdot(w, y);
                     const int rc = renorm(w, y, v);
                     if (lane == 0) {
@@ -331,7 +412,6 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
                 __syncthreads();
                 const int f2 = flag;
                 const bool tied = lam[1] >= lam[0] * (1.0 - 1e-9 * power);
-                __syncthreads();
                 if (tied) {
                     st = 1;
                     break;
