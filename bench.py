@@ -49,8 +49,8 @@ KERNEL_SRC = os.path.join(ROOT, "kv_cache_token_amd", "csrc", "kvx_device.hip")
 # copy) summarised in profiles/, valid only for the kernel source they were
 # taken on (sha256 prefix of kvx_device.hip).
 MEASURED_TRAFFIC = {
-    "c4": {"kernel_src_sha256_16": "53075be3be7412da", "bytes_per_launch": 977371162},
-    "c3": {"kernel_src_sha256_16": "53075be3be7412da", "bytes_per_launch": 9128218185},
+    "c4": {"kernel_src_sha256_16": "1e0b13b10d5f061b", "bytes_per_launch": 977375453},
+    "c3": {"kernel_src_sha256_16": "1e0b13b10d5f061b", "bytes_per_launch": 9128266344},
 }
 DESCRIPTIONS = {
     "c2": "c2_qfilters_calibrated: 28 layers x 8 KV heads x 128 (224 groups), bf16, one 4096-token block, "
@@ -474,6 +474,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle's sample until this much oracle time has run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the secondary measurements (per-layer launches, device copy rate), e.g. under a "
+                         "kernel trace whose per-kernel averages should cover the step's own launches only")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as one captured HIP graph (workloads without snapshots, one stream)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -559,13 +562,14 @@ def main():
         "head_tokens_per_s": round(value * cfg.L * cfg.H, 1),
         "step_algorithmic_GBps": round(step_gbps, 1), "step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
         "step_algorithmic_bytes": int(step_bytes),
-        "device_copy_GBps": copy_ceiling(torch, streams[0]),
+        "device_copy_GBps": None if args.no_extras else copy_ceiling(torch, streams[0]),
         "roofline": roof,
         "kernels": breakdown,
     }
     if args.workload == "c5":
         out["fallback_estimate"] = fallback_estimate_time(torch, wl)
-    if args.workload in ("c2", "c4") and args.streams == 1 and args.split == 1 and graph is None:
+    if args.workload in ("c2", "c4") and args.streams == 1 and args.split == 1 and graph is None \
+            and not args.no_extras:
         out["per_layer_ms_per_step"] = per_layer_ms(torch, wl, max(1, args.steps // 4))
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wl, args.cpu_groups, args.cpu_seconds)

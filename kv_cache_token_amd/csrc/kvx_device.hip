@@ -33,10 +33,13 @@ namespace {
 #ifndef KVX_SCORE_BLOCK
 #define KVX_SCORE_BLOCK 256
 #endif
-// Streaming (non-temporal) hints per kernel: K/V rows are touched once per
-// call, so they need not displace other data in the caches.
+// Streaming (non-temporal) hints per kernel: the compaction and the decode
+// shift touch their rows once per call, so they need not displace other data
+// in the caches.  Scoring reads the incoming keys with ordinary loads: the
+// compaction right after it re-reads the surviving new rows, and those still
+// in the last-level cache then come back without a trip to HBM.
 #ifndef KVX_SCORE_NT_LOAD
-#define KVX_SCORE_NT_LOAD 1
+#define KVX_SCORE_NT_LOAD 0
 #endif
 #ifndef KVX_GATHER_NT_LOAD
 #define KVX_GATHER_NT_LOAD 1
