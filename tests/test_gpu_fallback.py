@@ -292,3 +292,22 @@ def test_fallback_plan_replays_the_lifecycle():
         for x, y in zip(got, want):
             assert torch.equal(x, y), "replay %d" % rep
     assert torch.equal(c.filters, eager.filters)
+
+
+def test_failed_estimate_raises_eagerly_and_from_a_plan():
+    """Keys with no dominant direction (all rows equal) freeze nothing: the
+    eager update raises, and a plan reports it from check()."""
+    import torch
+    from kv_cache_token_amd.cache import EvictingCache
+    G, Dd = 8, 128
+    row = synth.custom_keys((1, 1, Dd), 21, "bf16")
+    K = np.tile(row, (G, 200, 1))
+    kt = synth.host_to_torch(K, "bf16").cuda()
+    c = EvictingCache(2, 1, 4, 64, 4, 0, mode="proj", calib_tokens=128)
+    with pytest.raises(RuntimeError, match="no dominant key direction"):
+        c.update(kt, kt)
+    c2 = EvictingCache(2, 1, 4, 64, 4, 0, mode="proj", calib_tokens=128)
+    plan = c2.plan([(kt, kt)])
+    plan.run()
+    with pytest.raises(RuntimeError, match="status 2"):
+        plan.check()

@@ -366,3 +366,31 @@ def test_invalid_arguments_are_rejected_before_launch():
     with pytest.raises(KvxError):         # and the library itself refuses a bad sign
         api.qf_score_keys(torch.zeros((2, 8, D), dtype=torch.bfloat16, device="cuda"), sh, 8, "proj",
                           torch.zeros((1, 2, D), device="cuda"), 3, s)
+
+
+def test_runs_are_deterministic():
+    """Two runs of the same stream (fresh caches, different streams) leave the
+    same bytes in every buffer, scores included (the pages' determinism check:
+    diffing two runs)."""
+    import torch
+    from kv_cache_token_amd.cache import EvictingCache
+    L, B, H, S = 4, 1, 8, 2048
+    cfg = synth.CONFIGS[4]
+    f = torch.from_numpy(synth.filters_mu(cfg)[:L]).cuda()
+    k = synth.host_to_torch(synth.custom_keys((L * B * H, 4 * S, D), 5, "bf16"), "bf16").cuda()
+    v = synth.host_to_torch(synth.custom_keys((L * B * H, 4 * S, D), 6, "bf16"), "bf16").cuda()
+    states = []
+    for rep in range(2):
+        st = torch.cuda.Stream()
+        for mode, keep, filt in (("l2", "low", None), ("proj", "high", f)):
+            c = EvictingCache(L, B, H, 3000, 4, 16, keep, mode, filt, -1, "bf16", stream=st)
+            with torch.cuda.stream(st):
+                for a in range(0, 4 * S, S):
+                    c.update(k[:, a:a + S], v[:, a:a + S])
+                for t in range(8):
+                    c.update(k[:, t:t + 1], v[:, t:t + 1])
+            torch.cuda.synchronize()
+            states.append([x.clone() for x in c.kept()])
+    for x, y in zip(states[:2], states[2:]):
+        for a, b in zip(x, y):
+            assert torch.equal(a, b)
