@@ -13,8 +13,6 @@ filter per group and runs the step over everything held.
 """
 from __future__ import annotations
 
-from typing import Optional
-
 import numpy as np
 
 from . import api
