@@ -483,7 +483,7 @@ def main():
                     help="also run one 1 GiB device copy (reference for byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        log("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run the same "
+        log("bench.py measures one GPU: the library has no multi-GPU path (each GPU would run the same "
             "step on its own groups); run with --gpus 1")
         sys.exit(2)
 
