@@ -68,6 +68,8 @@ extern "C" {
 /* Scorers. */
 #define KVX_SCORE_L2 0   /* s = ||k||_2                       */
 #define KVX_SCORE_PROJ 1 /* s = sign * (k . f[l][h])          */
+#define KVX_SCORE_CACHE_KEYS 0x100 /* or-ed into a mode: read the keys with
+                                      cache-allocating loads (see qf_score_keys) */
 
 /* Ranking direction. */
 #define KVX_KEEP_HIGH 0  /* keep the highest scores (projection; L2 ablation) */
@@ -122,6 +124,10 @@ KVX_API int kvx_abi_version(void);
  *            [L*B, H, D] are passed by describing the shape as L' = L*B, B' = 1.
  *   sign     +1 or -1 (projection only; ignored for L2)
  *   s_new    device [G, S] float32 output
+ * mode | KVX_SCORE_CACHE_KEYS reads the keys with cache-allocating loads
+ * instead of streaming ones.  It pays when the block's keys fit the 256 MB
+ * last-level cache and the compaction that follows will re-read a good share
+ * of them (the surviving new rows); the scores are the same either way.
  * Scores accumulate in float32 in a fixed order per row (independent of S and
  * of the launch), and a -0 result is written as +0.  Keys must be finite.
  * Errors: KVX_EINVAL (bad mode/sign/dtype/D, NULL pointer), KVX_ERANGE

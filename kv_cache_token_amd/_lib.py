@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libkvevict.so")
 
 KVX_OK, KVX_EINVAL, KVX_ERANGE, KVX_EDEVICE, KVX_EIO, KVX_EMISMATCH = 0, -1, -2, -3, -4, -5
 KVX_F32, KVX_BF16, KVX_F16 = 0, 1, 2
-KVX_SCORE_L2, KVX_SCORE_PROJ = 0, 1
+KVX_SCORE_L2, KVX_SCORE_PROJ, KVX_SCORE_CACHE_KEYS = 0, 1, 0x100
 KVX_KEEP_HIGH, KVX_KEEP_LOW = 0, 1
 KVX_HEAD_DIM, KVX_MAX_BUDGET, KVX_MAX_TOTAL, KVX_ONCHIP_TOTAL = 128, 1 << 21, 1 << 22, 32768
 

@@ -14,8 +14,8 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import (KVX_BF16, KVX_F16, KVX_F32, KVX_HEAD_DIM, KVX_KEEP_HIGH, KVX_KEEP_LOW, KVX_SCORE_L2,
-                   KVX_SCORE_PROJ, KvxParams, KvxShape, KvxStats, call)
+from ._lib import (KVX_BF16, KVX_F16, KVX_F32, KVX_HEAD_DIM, KVX_KEEP_HIGH, KVX_KEEP_LOW, KVX_SCORE_CACHE_KEYS,
+                   KVX_SCORE_L2, KVX_SCORE_PROJ, KvxParams, KvxShape, KvxStats, call)
 
 D = KVX_HEAD_DIM
 
@@ -104,14 +104,16 @@ def run_prepared(calls) -> None:
 
 
 def qf_score_keys(k_new, shape: KvxShape, S: int, mode, filters, sign: int, s_new, stream=None,
-                  prepare: bool = False):
-    """Score G*S incoming rows into s_new [G, S] (float32)."""
+                  prepare: bool = False, cache_keys: bool = False):
+    """Score G*S incoming rows into s_new [G, S] (float32); cache_keys reads the
+    keys with cache-allocating loads (KVX_SCORE_CACHE_KEYS)."""
     torch = _torch()
     G, m = _G(shape), mode_code(mode)
     kp = _dev(k_new, "k_new", torch_dtype(shape.dtype), G * S * shape.D)
     fp = _dev(filters, "filters", torch.float32, shape.L * shape.H * shape.D, allow_none=(m == KVX_SCORE_L2))
     sp = _dev(s_new, "s_new", torch.float32, G * S)
-    return _dispatch("qf_score_keys", (kp, shape, S, m, fp, sign, sp, _stream(stream)), prepare)
+    mf = m | KVX_SCORE_CACHE_KEYS if cache_keys else m
+    return _dispatch("qf_score_keys", (kp, shape, S, mf, fp, sign, sp, _stream(stream)), prepare)
 
 
 def kv_evict_workspace_size(shape: KvxShape, n_kept: int, S: int, params: KvxParams) -> int:

@@ -18,6 +18,7 @@ import numpy as np
 from . import api
 
 D = api.D
+LAST_LEVEL_CACHE_BYTES = 256 << 20   # MI355X's last-level (Infinity) cache
 
 
 class EvictingCache:
@@ -221,6 +222,17 @@ class EvictingCache:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws
 
+    def _cache_keys(self, S: int) -> bool:
+        """Whether scoring should leave the block's keys in the last-level
+        cache: they must fit it, and the compaction must be expected to re-read
+        at least a quarter of them (every row when nothing is evicted; about
+        budget / n_total of them otherwise)."""
+        row = self.D * (4 if self.dtype_name == "f32" else 2)
+        if self.G * S * row > 0.9 * LAST_LEVEL_CACHE_BYTES:
+            return False
+        n_total = self.n_kept + S
+        return n_total <= self.budget or 4 * self.budget >= n_total
+
     def _scores(self, S: int):
         import torch
         if self._s_new.shape[1] != S:
@@ -245,7 +257,7 @@ class EvictingCache:
             return self._crossing(k_new, v_new, S, prepare)
         s_new = self._scores(S)
         calls.append(api.qf_score_keys(k_new, self.score_shape, S, self.mode, self.filters, self.sign, s_new,
-                                       self.stream, prepare=prepare))
+                                       self.stream, prepare=prepare, cache_keys=self._cache_keys(S)))
         k, v, s, p = self._bufs[self._cur]
         nk, pos_base = self.n_kept, self.tokens_seen
         if S == 1:

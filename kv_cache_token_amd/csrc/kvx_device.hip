@@ -35,12 +35,9 @@ namespace {
 #endif
 // Streaming (non-temporal) hints per kernel: the compaction and the decode
 // shift touch their rows once per call, so they need not displace other data
-// in the caches.  Scoring reads the incoming keys with ordinary loads: the
-// compaction right after it re-reads the surviving new rows, and those still
-// in the last-level cache then come back without a trip to HBM.
-#ifndef KVX_SCORE_NT_LOAD
-#define KVX_SCORE_NT_LOAD 0
-#endif
+// in the caches.  Scoring streams the keys too unless the caller asks for
+// KVX_SCORE_CACHE_KEYS (the compaction will re-read many of them while they
+// still fit the last-level cache).
 #ifndef KVX_GATHER_NT_LOAD
 #define KVX_GATHER_NT_LOAD 1
 #endif
@@ -113,7 +110,7 @@ __device__ __forceinline__ float finish_score(int mode, float acc, float sign) {
 
 // Group-major tiles: block b scores rows [tile*RPB, tile*RPB + RPB) of group
 // b / tiles (used when a group has at least a tile of rows).
-template <int DT, int HD, int MODE, int U>
+template <int DT, int HD, int MODE, int U, bool NT>
 __global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_tile_kernel(
     const char *__restrict__ k, uint32_t S, uint32_t tiles, uint32_t BH, uint32_t H,
     const float *__restrict__ filt, float sign, float *__restrict__ out) {
@@ -132,7 +129,7 @@ __global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_tile_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t r = r0 + u * kRowsPerLoad + sub;
-        raw[u] = r < S ? ld16<KVX_SCORE_NT_LOAD>(kg + (size_t)r * R::kBytes + part * 16) : make_uint4(0, 0, 0, 0);
+        raw[u] = r < S ? ld16<NT>(kg + (size_t)r * R::kBytes + part * 16) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -144,7 +141,7 @@ __global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_tile_kernel(
 
 // Flat rows (a group has fewer rows than a tile, e.g. one decode token): row r
 // belongs to group r / S.
-template <int DT, int HD, int MODE, int U>
+template <int DT, int HD, int MODE, int U, bool NT>
 __global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_flat_kernel(
     const char *__restrict__ k, uint32_t n_rows, uint32_t S, uint32_t BH, uint32_t H,
     const float *__restrict__ filt, float sign, float *__restrict__ out) {
@@ -158,7 +155,7 @@ __global__ __launch_bounds__(KVX_SCORE_BLOCK) void score_flat_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t r = row0 + u * kRowsPerLoad + sub;
-        raw[u] = r < n_rows ? ld16<KVX_SCORE_NT_LOAD>(k + (size_t)r * R::kBytes + part * 16) : make_uint4(0, 0, 0, 0);
+        raw[u] = r < n_rows ? ld16<NT>(k + (size_t)r * R::kBytes + part * 16) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -775,30 +772,39 @@ int validate_select_sizes(const kvx_shape &shape, int64_t n_kept, int64_t S, con
 
 template <int DT, int HD, int MODE>
 int launch_score_mode(const void *k_new, int64_t G, const kvx_shape &sh, int64_t S, const float *filters,
-                      float sign, float *s_new, hipStream_t st) {
+                      float sign, float *s_new, bool cache_keys, hipStream_t st) {
     constexpr int U = KVX_SCORE_U;
     constexpr int kRowsPerBlock = (KVX_SCORE_BLOCK / 64) * (64 / Row<DT, HD>::kLanes) * U;
     const uint32_t BH = (uint32_t)(sh.B * sh.H), H = (uint32_t)sh.H;
     if (S >= kRowsPerBlock / 2) {
         const uint32_t tiles = (uint32_t)((S + kRowsPerBlock - 1) / kRowsPerBlock);
         if ((int64_t)tiles * G > INT32_MAX) return set_error(KVX_ERANGE, "qf_score_keys: grid too large");
-        score_tile_kernel<DT, HD, MODE, U><<<(uint32_t)(tiles * G), KVX_SCORE_BLOCK, 0, st>>>(
-            (const char *)k_new, (uint32_t)S, tiles, BH, H, filters, sign, s_new);
+        if (cache_keys)
+            score_tile_kernel<DT, HD, MODE, U, false><<<(uint32_t)(tiles * G), KVX_SCORE_BLOCK, 0, st>>>(
+                (const char *)k_new, (uint32_t)S, tiles, BH, H, filters, sign, s_new);
+        else
+            score_tile_kernel<DT, HD, MODE, U, true><<<(uint32_t)(tiles * G), KVX_SCORE_BLOCK, 0, st>>>(
+                (const char *)k_new, (uint32_t)S, tiles, BH, H, filters, sign, s_new);
     } else {
         const uint32_t n_rows = (uint32_t)(G * S);
         const uint32_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-        score_flat_kernel<DT, HD, MODE, U><<<blocks, KVX_SCORE_BLOCK, 0, st>>>(
-            (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, sign, s_new);
+        if (cache_keys)
+            score_flat_kernel<DT, HD, MODE, U, false><<<blocks, KVX_SCORE_BLOCK, 0, st>>>(
+                (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, sign, s_new);
+        else
+            score_flat_kernel<DT, HD, MODE, U, true><<<blocks, KVX_SCORE_BLOCK, 0, st>>>(
+                (const char *)k_new, n_rows, (uint32_t)S, BH, H, filters, sign, s_new);
     }
     return check_launch("qf_score_keys");
 }
 
 template <int DT, int HD>
 int launch_score(const void *k_new, int64_t G, const kvx_shape &sh, int64_t S, int32_t mode,
-                 const float *filters, int32_t sign, float *s_new, hipStream_t st) {
+                 const float *filters, int32_t sign, float *s_new, bool cache_keys, hipStream_t st) {
     if (mode == KVX_SCORE_L2)
-        return launch_score_mode<DT, HD, KVX_SCORE_L2>(k_new, G, sh, S, filters, 1.0f, s_new, st);
-    return launch_score_mode<DT, HD, KVX_SCORE_PROJ>(k_new, G, sh, S, filters, (float)sign, s_new, st);
+        return launch_score_mode<DT, HD, KVX_SCORE_L2>(k_new, G, sh, S, filters, 1.0f, s_new, cache_keys, st);
+    return launch_score_mode<DT, HD, KVX_SCORE_PROJ>(k_new, G, sh, S, filters, (float)sign, s_new, cache_keys,
+                                                     st);
 }
 
 template <int DT, int HD>
@@ -834,8 +840,12 @@ KVX_API int qf_score_keys(const void *k_new, kvx_shape shape, int64_t S, int32_t
     int rc = check_shape(shape, &G);
     if (rc) return rc;
     if (S < 0) return set_error(KVX_EINVAL, "qf_score_keys: S must be >= 0");
+    const bool cache_keys = (mode & KVX_SCORE_CACHE_KEYS) != 0;
+    if (cache_keys) mode &= ~KVX_SCORE_CACHE_KEYS;
     if (mode != KVX_SCORE_L2 && mode != KVX_SCORE_PROJ)
-        return set_error(KVX_EINVAL, "qf_score_keys: mode must be KVX_SCORE_L2 or KVX_SCORE_PROJ (got %d)", (int)mode);
+        return set_error(KVX_EINVAL,
+                         "qf_score_keys: mode must be KVX_SCORE_L2 or KVX_SCORE_PROJ, optionally | "
+                         "KVX_SCORE_CACHE_KEYS (got %d)", (int)mode);
     if (mode == KVX_SCORE_PROJ && sign != 1 && sign != -1)
         return set_error(KVX_EINVAL, "qf_score_keys: sign must be +1 or -1 (got %d)", (int)sign);
     if (mode == KVX_SCORE_PROJ && filters == nullptr)
@@ -846,7 +856,7 @@ KVX_API int qf_score_keys(const void *k_new, kvx_shape shape, int64_t S, int32_t
     hipStream_t st = (hipStream_t)stream;
     return dispatch_row(shape, false, [&](auto dt, auto hd) {
         return launch_score<decltype(dt)::value, decltype(hd)::value>(k_new, G, shape, S, mode, filters, sign,
-                                                                       s_new, st);
+                                                                       s_new, cache_keys, st);
     });
 }
 

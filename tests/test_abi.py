@@ -61,6 +61,8 @@ def test_validation_rejects_bad_calls_without_launching():
         ("qf_score_keys", (FAKE, sh, 10, 1, None, 1, FAKE, None), -1),
         ("qf_score_keys", (FAKE, sh, 10, 1, FAKE, 2, FAKE, None), -1),
         ("qf_score_keys", (FAKE, sh, 10, 9, FAKE, 1, FAKE, None), -1),
+        ("qf_score_keys", (FAKE, sh, 10, 0x200, FAKE, 1, FAKE, None), -1),
+        ("qf_score_keys", (FAKE, sh, 10, 0x102, FAKE, 1, FAKE, None), -1),
         ("qf_score_keys", (FAKE, api.KvxShape(2, 1, 4, 128, 1), 2 ** 30, 0, None, 1, FAKE, None), -2),
         ("kv_compact_gather", (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, sh, 10, 10, ok,
                                FAKE, ctypes.c_void_p(0x2000), FAKE, FAKE, None), -1),      # partial alias

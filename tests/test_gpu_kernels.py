@@ -394,3 +394,26 @@ def test_runs_are_deterministic():
     for x, y in zip(states[:2], states[2:]):
         for a, b in zip(x, y):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mode,sign", [("l2", 1), ("proj", -1)])
+def test_score_cache_hint_changes_nothing_but_the_loads(mode, sign):
+    """mode | KVX_SCORE_CACHE_KEYS gives the same scores bit for bit, on the
+    tile path and the flat (decode) path."""
+    import torch
+    api = _api()
+    L, B, H = 2, 1, 4
+    G = L * B * H
+    rng = np.random.default_rng(12)
+    f = rng.standard_normal((L, H, D)).astype(np.float32)
+    fd = torch.from_numpy(f).cuda() if mode == "proj" else None
+    for S in (1000, 1):
+        K = synth.custom_keys((G, S, D), 30 + S, "bf16")
+        kt = _t(K, "bf16")
+        outs = []
+        for hint in (False, True):
+            out = torch.full((G, S), float("nan"), dtype=torch.float32, device="cuda")
+            api.qf_score_keys(kt, api.make_shape(L, B, H, "bf16"), S, mode, fd, sign, out, cache_keys=hint)
+            outs.append(out)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1])
