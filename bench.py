@@ -49,10 +49,10 @@ KERNEL_SRC = os.path.join(ROOT, "kv_cache_token_amd", "csrc", "kvx_device.hip")
 # copy) summarised in profiles/, valid only for the kernel source they were
 # taken on (sha256 prefix of kvx_device.hip).
 MEASURED_TRAFFIC = {
-    "c4": {"kernel_src_sha256_16": "c86fa0c85b1ce942", "bytes_per_launch": 977354704},
-    "c3": {"kernel_src_sha256_16": "c86fa0c85b1ce942", "bytes_per_launch": 9128283754},
-    "c5": {"kernel_src_sha256_16": "c86fa0c85b1ce942", "bytes_per_launch": 2230725153},
-    "c2": {"kernel_src_sha256_16": "c86fa0c85b1ce942", "bytes_per_launch": 123578537},
+    "c4": {"kernel_src_sha256_16": "acc63fda78ec5436", "bytes_per_launch": 964537794},
+    "c3": {"kernel_src_sha256_16": "acc63fda78ec5436", "bytes_per_launch": 9128369775},
+    "c5": {"kernel_src_sha256_16": "acc63fda78ec5436", "bytes_per_launch": 2202137524},
+    "c2": {"kernel_src_sha256_16": "acc63fda78ec5436", "bytes_per_launch": 122609076},
 }
 DESCRIPTIONS = {
     "c2": "c2_qfilters_calibrated: 28 layers x 8 KV heads x 128 (224 groups), bf16, one 4096-token block, "

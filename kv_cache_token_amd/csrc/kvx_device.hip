@@ -28,7 +28,7 @@ namespace {
 #define KVX_GATHER_U 1
 #endif
 #ifndef KVX_GATHER_BLOCK
-#define KVX_GATHER_BLOCK 256
+#define KVX_GATHER_BLOCK 1024
 #endif
 #ifndef KVX_SCORE_BLOCK
 #define KVX_SCORE_BLOCK 256
