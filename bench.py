@@ -25,7 +25,13 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                prefill, the in-place decode kernel for c3): algorithmic bytes
                per launch over its mean duration from HIP events recorded on the
                launch stream around every call, in a second timed pass
-  cpu_baseline the oracle (plain C, OpenMP) on a sample of the same workload
+  cpu_baseline the oracle (plain C, OpenMP) on a sample of the same workload,
+               repeated to about 10 s, with its single-thread rate beside
+  beside them  head_tokens_per_s, the step's algorithmic GB/s, the kernels'
+               mean launch times, the library's own device-copy rate and (c2,
+               c4) the same step launched layer by layer; --no-extras skips the
+               last two.  --streams / --split run independent caches
+               concurrently (the default line uses one stream).
 """
 from __future__ import annotations
 
