@@ -1,0 +1,30 @@
+"""bench.py's host-side parts on the CPU: the one-GPU guard and the oracle
+baseline leg (the GPU legs run on the device only)."""
+import os
+import subprocess
+import sys
+import types
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=300)
+    assert out.returncode == 2
+    assert "one GPU" in out.stderr and out.stdout == ""
+
+
+@pytest.mark.parametrize("cid", [4, 3])
+def test_oracle_baseline_leg_reports_its_sample(cid):
+    import bench
+    from kv_cache_token_amd import synth
+    cfg = synth.CONFIGS[cid]
+    tokens = len(cfg.scorers) * cfg.B * (256 if cid == 3 else cfg.tokens)
+    wl = types.SimpleNamespace(cfg=cfg, tokens_per_step=tokens)
+    cb = bench.cpu_baseline(wl, 2, min_seconds=0.2)
+    assert cb["kind"] == "oracle" and cb["unit"] == "tokens/s" and cb["value"] > 0
+    assert cb["value_1_thread"] > 0 and cb["cores"] >= 1
+    assert "2 of %d groups" % cfg.G in cb["sample"]
