@@ -449,7 +449,7 @@ def bench_qcal(torch, args):
         "vs_baseline": None, "dtype": "f64",
         "data": "synthetic (seeded, HBM-resident; rows drift*mu_h + N(0,0.25), heads of a KV group leaning together)",
         "config": {"workload": DESCRIPTIONS["qcal"], "device": torch.cuda.get_device_name(0)},
-        "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP64_TFLOPS, 4), "traffic": None,
                      "kernel": "top_direction_kernel (Gram flops only)",
                      "algorithmic_flops_per_launch": int(flops), "mean_launch_us": round(ms * 1e3, 1)},
