@@ -205,47 +205,66 @@ struct SelRows {
     int n_kept, n_total, n_sink, recent, keep_low;
 };
 
-__device__ __forceinline__ uint32_t row_key(const SelRows &a, int r) {
-    const float s = r < a.n_kept ? a.sk[r] : a.sn[r - a.n_kept];
-    const bool prot = r < a.n_sink || r >= a.n_total - a.recent;
-    return prot ? 0xFFFFFFFFu : select_key(s, a.keep_low);
-}
-
 // Load the keys of rows r0 + i*NT + t, i < M (rows past n_total get key 0 and
-// are never counted).
+// are never counted).  Every load is issued before any is used: rows past the
+// end read the last row instead, and the source array is picked by address,
+// so no branch separates the loads.
 template <int M, int NT>
 __device__ __forceinline__ void load_keys(const SelRows &a, int r0, uint32_t *key) {
+    float s[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int r = min(r0 + i * NT + (int)threadIdx.x, a.n_total - 1);
+        s[i] = *(r < a.n_kept ? a.sk + r : a.sn + (r - a.n_kept));
+    }
 #pragma unroll
     for (int i = 0; i < M; ++i) {
         const int r = r0 + i * NT + (int)threadIdx.x;
-        key[i] = r < a.n_total ? row_key(a, r) : 0u;
+        const bool prot = r < a.n_sink || r >= a.n_total - a.recent;
+        key[i] = r < a.n_total ? (prot ? 0xFFFFFFFFu : select_key(s[i], a.keep_low)) : 0u;
     }
 }
 
 // Count the digit (key >> shift) & 255 of every key that matches the prefix
-// into this wave's 256-bin LDS histogram h.  While one digit covers many lanes
-// the increments are aggregated per wave; once digits spread, one per lane.
+// into this wave's 256-bin LDS histogram h.  In the first pass every key
+// counts and scores cluster in a few top digits, so each lane first sums its
+// own equal digits (eight keys at a time, plain vector compares) and adds
+// each distinct digit once; in later passes few keys are left, spread over
+// more digits, and each adds itself.  (Merging equal digits across a wave with
+// ballots costs scalar instructions that the CU's 16 waves share, and was
+// slower in both cases.)
 template <int M, int NT>
 __device__ __forceinline__ void count_digits(const uint32_t *key, int r0, int n_total, uint32_t prefix,
                                              uint32_t pmask, int shift, uint32_t *h) {
-    const int lane = threadIdx.x & 63;
+    if (pmask != 0) {
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-        const int r = r0 + i * NT + (int)threadIdx.x;
-        bool act = r < n_total && (key[i] & pmask) == prefix;
-        const uint32_t d = (key[i] >> shift) & 0xFFu;
-        for (int it = 0; it < 4; ++it) {
-            const uint64_t am = __ballot(act);
-            if (am == 0) break;
-            const int leader = __ffsll((unsigned long long)am) - 1;
-            const uint32_t ld = __builtin_amdgcn_readlane(d, leader);
-            const bool mine = act && d == ld;
-            const uint32_t cnt = (uint32_t)__popcll(__ballot(mine));
-            if (lane == leader) atomicAdd(&h[ld], cnt);
-            if (mine) act = false;
-            if (cnt < 8) break;
+        for (int i = 0; i < M; ++i) {
+            const int r = r0 + i * NT + (int)threadIdx.x;
+            if (r < n_total && (key[i] & pmask) == prefix) atomicAdd(&h[(key[i] >> shift) & 0xFFu], 1u);
         }
-        if (act) atomicAdd(&h[d], 1u);
+        return;
+    }
+    constexpr int W = M < 8 ? M : 8;
+#pragma unroll
+    for (int w0 = 0; w0 < M; w0 += W) {
+        uint32_t d[W];
+        bool act[W];
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            act[i] = r0 + (w0 + i) * NT + (int)threadIdx.x < n_total;
+            d[i] = (key[w0 + i] >> shift) & 0xFFu;
+        }
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            uint32_t c = 1;
+#pragma unroll
+            for (int j = i + 1; j < W; ++j) {
+                const bool same = act[i] && act[j] && d[j] == d[i];
+                c += same;
+                act[j] = act[j] && !same;
+            }
+            if (act[i]) atomicAdd(&h[d[i]], c);
+        }
     }
 }
 

@@ -3,7 +3,8 @@
 score: bit-exact on exactly representable inputs, within 1e-5 of the condition
 scale otherwise, and independent of how a block is split.  select: keep_idx
 bit-exact against the oracle's ranking on the same scores, across tile
-boundaries, ties, signed zeros, real infinities and the largest sizes.
+boundaries, ties, signed zeros, real infinities, the largest sizes, and
+threshold bins of 1 to 513 keys isolated at each radix pass.
 gather / decode: bit-exact against a plain numpy gather / the oracle's rules.
 """
 import zlib
@@ -222,6 +223,42 @@ def test_large_budget_stream_lockstep_with_oracle():
         assert np.array_equal(s[g].cpu().numpy(), os_)
         assert np.array_equal(synth.torch_to_host(k[g], "bf16"), ok)
         assert np.array_equal(synth.torch_to_host(v[g], "bf16"), ov)
+
+
+def _bin_boundary_scores(stage, nb, rng):
+    """Scores whose budget-th best lies in a radix bin of exactly nb keys at
+    pass `stage` (0, 1 or 2), all earlier bins being larger, the bin's keys
+    equal above their low byte (so its rows are told apart only by the last
+    pass, and by the row order on ties).  Returns (scores in a random row
+    order, budget)."""
+    parts = [np.full(500, 1.75)]                           # above, same top byte from stage 1 on
+    b = 1.25 + (np.arange(nb) % 256) * 2.0 ** -23          # the bin: equal above the low byte
+    if stage == 0:
+        parts = [np.full(500, 100.0), np.full(400, 0.01)]  # other top bytes
+    elif stage == 1:
+        parts.append(np.full(400, 1.0))                    # same top byte, lower stage-1 bin
+    else:
+        parts += [np.full(600, 1.25 + 2.0 ** -12), np.full(400, 1.0)]  # same stage-1 bin, higher stage-2 bin
+    above = 500 + (600 if stage == 2 else 0)
+    s = np.concatenate(parts + [b]).astype(np.float32)
+    return s[rng.permutation(len(s))], above + max(1, nb // 2)
+
+
+@pytest.mark.parametrize("stage", [0, 1, 2])
+@pytest.mark.parametrize("nb", [1, 64, 65, 511, 512, 513])
+@pytest.mark.parametrize("keep", ["high", "low"])
+def test_select_threshold_bin_sizes_at_each_pass(stage, nb, keep):
+    rng = np.random.default_rng(100 * stage + nb)
+    rows = [_bin_boundary_scores(stage, nb, rng) for _ in range(2)]
+    assert rows[0][1] == rows[1][1]
+    budget = rows[0][1]
+    s = np.stack([r[0] for r in rows])
+    if keep == "low":
+        s = -s
+    n_kept = 300
+    idx = _select_gpu(s[:, :n_kept], s[:, n_kept:], n_kept, s.shape[1] - n_kept, budget, 0, 0, keep)
+    for g in range(2):
+        assert np.array_equal(idx[g], oracle.select(s[g], budget, 0, 0, keep)), g
 
 
 def test_select_real_infinities_rank_below_protected_rows():
