@@ -355,16 +355,18 @@ __device__ __forceinline__ void write_kept(const uint32_t *key, int r0, int n_to
 }
 
 // One workgroup of NT threads per group; thread t holds the keys of rows
-// t, t + NT, ... (M of them) in registers, so every load is coalesced.  Each
-// wave counts into its own LDS histogram (scores cluster, so a shared one would
-// serialise the waves on a few bins); the next pass's histograms are cleared
-// while the current one is scanned.
+// t, t + NT, ... (M of them) in registers, so every load is coalesced.  All
+// waves count into one LDS histogram: the LDS runs one wave's atomics at a
+// time anyway, and what costs is many lanes of one instruction on one bin,
+// which count_digits avoids where scores cluster.  The next pass's histogram
+// is cleared while the current one is scanned.
 template <int M, int NT>
 __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_kept,
                                                       const float *__restrict__ s_new, int n_kept,
                                                       int S, int budget, int n_sink, int recent,
                                                       int keep_low, int32_t *__restrict__ keep_idx) {
     constexpr int NW = NT / 64;
+    static_assert(NW >= 2, "wave 1 clears the histograms while wave 0 scans");
     const int g = blockIdx.x;
     const int t = threadIdx.x, w = t >> 6;
     const int n_total = n_kept + S;
@@ -376,40 +378,32 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
     const SelRows rows{s_kept + (size_t)g * budget, s_new + (size_t)g * S, n_kept, n_total, n_sink, recent,
                        keep_low};
 
-    __shared__ uint4 hist4[2][NW][64];  // per-wave 256-bin histograms, two passes' worth
+    __shared__ uint4 hist4[2][64];  // 256-bin histograms, two passes' worth
     __shared__ uint32_t sel[2];
     __shared__ uint32_t chunk[M * NW];
-    uint32_t(*hist)[NW][256] = reinterpret_cast<uint32_t(*)[NW][256]>(hist4);
+    uint32_t(*hist)[256] = reinterpret_cast<uint32_t(*)[256]>(hist4);
 
     uint32_t key[M];
     load_keys<M, NT>(rows, 0, key);
-    for (int i = t; i < NW * 64; i += NT) (&hist4[0][0][0])[i] = make_uint4(0, 0, 0, 0);
+    if (t < 64) hist4[0][t] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
     uint32_t prefix = 0, pmask = 0, krem = (uint32_t)budget;
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        count_digits<M, NT>(key, 0, n_total, prefix, pmask, shift, hist[pass & 1][w]);
+        count_digits<M, NT>(key, 0, n_total, prefix, pmask, shift, hist[pass & 1]);
         __syncthreads();
         if (w == 0) {
-            uint4 c = make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < NW; ++v) {
-                const uint4 x = hist4[pass & 1][v][63 - (t & 63)];
-                c.x += x.x;
-                c.y += x.y;
-                c.z += x.z;
-                c.w += x.w;
-            }
+            const uint4 c = hist4[pass & 1][63 - t];
             uint32_t d, nk;
             if (pick_digit(c, krem, &d, &nk)) {
                 sel[0] = d;
                 sel[1] = nk;
             }
         }
-        if (pass < 3)  // clear the other histograms for the next pass meanwhile
-            for (int i = t; i < NW * 64; i += NT) (&hist4[(pass + 1) & 1][0][0])[i] = make_uint4(0, 0, 0, 0);
+        if (pass < 3 && w == 1)  // wave 1 clears the next pass's histogram meanwhile
+            hist4[(pass + 1) & 1][t - 64] = make_uint4(0, 0, 0, 0);
         __syncthreads();
         prefix |= sel[0] << shift;
         pmask |= 0xFFu << shift;
