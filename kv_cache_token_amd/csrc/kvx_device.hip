@@ -293,6 +293,11 @@ __device__ __forceinline__ bool pick_digit(uint4 c, uint32_t krem, uint32_t *dig
     return true;
 }
 
+// Number of set bits of m in the lanes below this one (v_mbcnt).
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Write the kept rows among rows r0 + i*NT + t (i < M) in row order:
 // out[base_gt + #(key > tau before) + min(base_eq + #(key == tau before), quota)].
 // `chunk` holds M*NT/64 counters.  Ends with the block synchronised.
@@ -329,27 +334,23 @@ __device__ __forceinline__ void write_kept(const uint32_t *key, int r0, int n_to
         }
     }
     __syncthreads();
-    const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
         const int c = i * NW + w;
         const int r = r0 + c * 64 + lane;
         const bool valid = r < n_total;
-        const uint64_t gm = __ballot(valid && key[i] > tau);
-        const uint64_t em = __ballot(valid && key[i] == tau);
-        if (valid) {
-            const uint32_t base = chunk[c];
-            const uint32_t gb = base_gt + (base >> 16) + (uint32_t)__popcll(gm & below);
-            const uint32_t eb = base_eq + (base & 0xFFFFu) + (uint32_t)__popcll(em & below);
-            // Exactly `budget` rows qualify, so every slot is below budget; the
-            // bound check only keeps a corrupt input from writing past the row.
-            uint32_t slot = 0xFFFFFFFFu;
-            if (key[i] > tau)
-                slot = gb + min(eb, quota);
-            else if (key[i] == tau && eb < quota)
-                slot = gb + eb;
-            if (slot < (uint32_t)budget) out[slot] = r;
-        }
+        const bool gt = valid && key[i] > tau, eq = valid && key[i] == tau;
+        const uint32_t base = chunk[c];
+        const uint32_t gb = base_gt + (base >> 16) + lanes_below(__ballot(gt));
+        const uint32_t eb = base_eq + (base & 0xFFFFu) + lanes_below(__ballot(eq));
+        // Exactly `budget` rows qualify, so every slot is below budget; the
+        // bound check only keeps a corrupt input from writing past the row.
+        uint32_t slot = 0xFFFFFFFFu;
+        if (gt)
+            slot = gb + min(eb, quota);
+        else if (eq && eb < quota)
+            slot = gb + eb;
+        if (slot < (uint32_t)budget) out[slot] = r;
     }
     __syncthreads();
 }
