@@ -145,6 +145,7 @@ class Workload:
         self._turn = 0
         torch.cuda.synchronize()
         self.tokens_per_step = len(cfg.scorers) * cfg.B * sum(b[0].shape[1] for b in self.blocks)
+        self.calls_per_step = sum(len(p.calls) for p in self.plans)
         self.dominant = "kv_evict_one_inplace" if cid == 3 else "kv_compact_gather"
 
     def restore(self):
@@ -228,6 +229,14 @@ def algorithmic_bytes(torch, wl):
     return total, dom
 
 
+def hold(torch, stream, n_calls):
+    """Keep `stream` busy (a spin kernel, about 30 us per call to come, outside
+    any timed interval) so that the host has enqueued the calls before the GPU
+    reaches them: the events then time the GPU's work, not host gaps."""
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(min(max(n_calls, 30), 2000) * 30e-6 * 2.4e9))
+
+
 def timed_steps(torch, wl, n, graph=None):
     """Mean milliseconds per step over n steps.  Without snapshots the steps run
     back to back between two events; with snapshots every step is bracketed by
@@ -237,6 +246,7 @@ def timed_steps(torch, wl, n, graph=None):
 
     def bracket(k):
         start, end = ev(enable_timing=True), ev(enable_timing=True)
+        hold(torch, s0, k * wl.calls_per_step)
         start.record(s0)
         for s in rest:
             s.wait_event(start)
@@ -278,6 +288,7 @@ def kernel_times(torch, wl, steps):
         torch.cuda.synchronize()
         for p in wl.plan_sets[s % len(wl.plan_sets)]:
             rec = []
+            hold(torch, p.cache.stream, len(p.calls))
 
             def hook(i, name, when, p=p, rec=rec):
                 e = ev(enable_timing=True)
@@ -393,13 +404,15 @@ def per_layer_ms(torch, wl, steps):
                               cfg.dtype, stream=st)
             plans.append(c.plan([(k[l * bh:(l + 1) * bh], v[l * bh:(l + 1) * bh]) for k, v in wl.blocks]))
     run = lambda: [p.run() for p in plans]  # noqa: E731
-    event_times(torch, st, run, 1)
-    return round(event_times(torch, st, run, steps), 4)
+    n_calls = sum(len(p.calls) for p in plans)
+    event_times(torch, st, run, 1, n_calls)
+    return round(event_times(torch, st, run, steps, n_calls), 4)
 
 
-def event_times(torch, stream, fn, n):
+def event_times(torch, stream, fn, n, calls_per_fn=1):
     """Mean milliseconds of fn() over n launches, from HIP events on `stream`."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    hold(torch, stream, n * calls_per_fn)
     with torch.cuda.stream(stream):
         for a, b in ev:
             a.record(stream)
