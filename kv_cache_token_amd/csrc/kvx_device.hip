@@ -440,26 +440,20 @@ __device__ __forceinline__ SelRows mb_rows(const MbArgs &a, int g) {
 // Histogram of one radix pass over one row block, added into the group's
 // workspace histogram.
 __global__ __launch_bounds__(MB_NT) void mb_hist_kernel(MbArgs a, int shift) {
-    constexpr int NW = MB_NT / 64;
     const int g = blockIdx.x / a.W, blk = blockIdx.x - g * a.W;
-    const int t = threadIdx.x, w = t >> 6;
+    const int t = threadIdx.x;
     uint32_t *ws = a.ws + (size_t)g * mb_words(a.W);
     const uint32_t prefix = ws[256], pmask = ws[257];
-    __shared__ uint32_t hist[NW][256];
-    for (int i = t; i < NW * 256; i += MB_NT) (&hist[0][0])[i] = 0;
+    __shared__ uint32_t hist[256];
+    if (t < 256) hist[t] = 0;
     __syncthreads();
     uint32_t key[MB_M];
     const SelRows rows = mb_rows(a, g);
     const int r0 = blk * MB_ROWS;
     load_keys<MB_M, MB_NT>(rows, r0, key);
-    count_digits<MB_M, MB_NT>(key, r0, rows.n_total, prefix, pmask, shift, hist[w]);
+    count_digits<MB_M, MB_NT>(key, r0, rows.n_total, prefix, pmask, shift, hist);
     __syncthreads();
-    if (t < 256) {
-        uint32_t s = 0;
-#pragma unroll
-        for (int v = 0; v < NW; ++v) s += hist[v][t];
-        if (s) atomicAdd(&ws[t], s);
-    }
+    if (t < 256 && hist[t]) atomicAdd(&ws[t], hist[t]);
 }
 
 // One wave per group: choose the digit of this pass, advance the state and
