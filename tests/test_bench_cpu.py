@@ -28,3 +28,24 @@ def test_oracle_baseline_leg_reports_its_sample(cid):
     assert cb["kind"] == "oracle" and cb["unit"] == "tokens/s" and cb["value"] > 0
     assert cb["value_1_thread"] > 0 and cb["cores"] >= 1
     assert "2 of %d groups" % cfg.G in cb["sample"]
+
+
+def test_measured_traffic_matches_the_committed_counter_summaries():
+    """bench.py's per-launch HBM traffic figures are the ones the committed
+    rocprofv3 counter summaries derive, for the same kernel source hash."""
+    import glob
+    import re
+    import bench
+    names = {"c4": "c4_chunked_prefill_32k", "c3": "c3_decode_stream", "c5": "c5_keysvd_fallback_128k",
+             "c2": "c2_qfilters_calibrated"}
+    assert set(bench.MEASURED_TRAFFIC) == set(names)
+    assert len(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_counters.md"))) == len(names)
+    for w, stem in names.items():
+        text = open(os.path.join(ROOT, "profiles", stem + "_hbm_counters.md")).read()
+        sha = re.search(r"Kernel source sha256\[:16\]: `([0-9a-f]{16})`", text).group(1)
+        dom = int(re.search(r"Dominant kernel \(.*\): (\d+) calibrated HBM bytes per launch", text).group(1))
+        mt = bench.MEASURED_TRAFFIC[w]
+        assert mt["kernel_src_sha256_16"] == sha, w
+        assert abs(mt["bytes_per_launch"] - dom) <= 1, w
+        trace = open(os.path.join(ROOT, "profiles", stem + "_kernel_stats.md")).read()
+        assert "`%s`" % sha in trace, w
