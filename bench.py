@@ -17,7 +17,10 @@ tokens in 8192-token chunks, budget 8192, key-SVD fallback filters estimated
 before the timed region; the estimate's own time is reported beside), qcal (the
 query-SVD calibration of a 28-layer model with 24 query heads over 8 KV heads,
 3000 samples per query head, on the device; a once-per-model step outside the
-eviction path, reported with its own metric).
+eviction path, reported with its own metric).  --dtype, --head-dim, --budget,
+--chunk and --tokens run a prefill workload's recipe at other sizes (fp16 or
+fp32 K/V, head dims 64 and 256, budgets past the on-chip selection); the
+variant is named in config.workload.
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
   value        tokens absorbed per second over the whole step (all runs)
@@ -48,7 +51,6 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 D = 128
-ROW = D * 2  # bytes of one bf16 K or V row
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_token_amd", "csrc", "kvx_device.hip")
 # Calibrated HBM bytes per launch of the dominant kernel, from the two rocprofv3
 # counter runs (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; factors from a 1 GiB device
@@ -86,12 +88,13 @@ class Workload:
     each run's groups are divided by layer into that many independent caches
     (the step is per group), spread over the streams."""
 
-    def __init__(self, torch, name, streams, split=1):
+    def __init__(self, torch, name, streams, split=1, cfg=None):
         from kv_cache_token_amd import synth
         from kv_cache_token_amd.cache import EvictingCache
         cid = int(name[1:])
-        self.name, self.cfg, self.streams = name, synth.CONFIGS[cid], streams
+        self.name, self.cfg, self.streams = name, cfg or synth.CONFIGS[cid], streams
         cfg = self.cfg
+        self.row = cfg.D * (4 if cfg.dtype == "f32" else 2)   # bytes of one K or V row
         with torch.cuda.stream(streams[0]):
             mus = synth.device_mus(cfg) if cfg.keys == "aniso" else None
             if cid == 3:
@@ -119,7 +122,7 @@ class Workload:
                 st = streams[(i * split + p) % len(streams)]
                 c = EvictingCache(per, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode,
                                   f_mu[l0:l1] if sc.filt == "mu" else None, sc.sign, cfg.dtype, stream=st,
-                                  calib_tokens=cfg.calib_tokens, calib_keys=cfg.calib_keys)
+                                  calib_tokens=cfg.calib_tokens, calib_keys=cfg.calib_keys, head_dim=cfg.D)
                 blocks = part(self.blocks, l0, l1)
                 with torch.cuda.stream(st):
                     if sc.filt == "keysvd":       # freeze the fallback filters once, outside the timed step
@@ -178,6 +181,7 @@ def algorithmic_bytes(torch, wl):
     row read and written (2*(2*Row+8)), the candidate scores read (4 B each),
     the incoming row read and written (2*Row+4 + 2*Row+8)."""
     total, dom = 0, []
+    ROW = wl.row
     wl.restore()
     for cache, plan in zip(wl.caches, wl.plans):
         st = {"n_kept": plan.start[0], "S": 0, "pos": None}
@@ -332,9 +336,9 @@ def cpu_baseline(wl, n_groups, min_seconds=10.0):
             f_lh = synth.filters_mu(cfg)
             fs = np.stack([f_lh[cfg.group_lbh(g)[0], cfg.group_lbh(g)[2]] for g in sample])
         elif sc.filt == "keysvd":
-            k0 = synth.bf16_bits_to_f32(chunks[0][0][:, :cfg.calib_tokens]).astype(np.float64)
+            k0 = synth.bits_to_f32(chunks[0][0][:, :cfg.calib_tokens], cfg.dtype).astype(np.float64)
             fs = np.stack([calib.estimate_filter_dir(k0[i]) for i in range(len(sample))]).astype(np.float32)
-        oc = oracle.OracleCache(len(sample), D, cfg.dtype, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode,
+        oc = oracle.OracleCache(len(sample), cfg.D, cfg.dtype, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode,
                                 fs, sc.sign)
         if cfg.cid == 3:
             oc.update(*pre)               # the decode step starts from a full cache (untimed)
@@ -428,7 +432,7 @@ def fallback_estimate_time(torch, wl):
     from kv_cache_token_amd import api
     cfg, st = wl.cfg, wl.streams[0]
     k0 = wl.blocks[0][0]
-    f = torch.empty((cfg.G, D), dtype=torch.float32, device="cuda")
+    f = torch.empty((cfg.G, cfg.D), dtype=torch.float32, device="cuda")
     status = torch.empty(cfg.G, dtype=torch.int32, device="cuda")
     fn = lambda: api.qf_filters_from_keys_device(k0, cfg.G, cfg.calib_tokens, k0.shape[1], f, status,  # noqa: E731
                                                  stream=st)
@@ -481,6 +485,37 @@ def bench_qcal(torch, args):
     print(json.dumps(out_line), flush=True)
 
 
+def variant_config(args):
+    """The workload's config with the variant options applied, and a text
+    naming them ("" when none is given)."""
+    import dataclasses
+    from kv_cache_token_amd import synth
+    opts = {k: getattr(args, k) for k in ("dtype", "head_dim", "budget", "chunk", "tokens")
+            if getattr(args, k) is not None}
+    if args.workload == "qcal" and not opts:
+        return None, ""
+    if opts and args.workload not in ("c2", "c4", "c5"):
+        log("size variants apply to the prefill workloads c2, c4 and c5")
+        sys.exit(2)
+    cfg = synth.CONFIGS[int(args.workload[1:])]
+    if not opts:
+        return cfg, ""
+    chunk = opts.get("chunk", cfg.chunks[0])
+    tokens = opts.get("tokens", cfg.tokens)
+    if tokens % chunk or chunk < 1:
+        log("--tokens must be a positive multiple of --chunk")
+        sys.exit(2)
+    head_dim = opts.get("head_dim", cfg.D)
+    if head_dim == 256 and any(sc.filt == "keysvd" for sc in cfg.scorers):
+        log("the key-SVD fallback estimates filters on the device for head dims 64 and 128 only")
+        sys.exit(2)
+    cfg = dataclasses.replace(cfg, dtype=opts.get("dtype", cfg.dtype), D=head_dim,
+                              budget=opts.get("budget", cfg.budget), chunks=(chunk,) * (tokens // chunk))
+    text = "variant: %s K/V, head_dim %d, budget %d, %d tokens per run in %d-token chunks" % (
+        cfg.dtype, cfg.D, cfg.budget, tokens, chunk)
+    return cfg, text
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -502,11 +537,18 @@ def main():
                     help="replay each step as one captured HIP graph (workloads without snapshots, one stream)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference for byte counters)")
+    vg = ap.add_argument_group("variants of a prefill workload (c2, c4, c5): the same recipe with other sizes")
+    vg.add_argument("--dtype", choices=("bf16", "f16", "f32"), help="K/V element type")
+    vg.add_argument("--head-dim", type=int, choices=(64, 128, 256))
+    vg.add_argument("--budget", type=int, help="rows kept per group")
+    vg.add_argument("--chunk", type=int, help="tokens per call")
+    vg.add_argument("--tokens", type=int, help="tokens per run (a multiple of the chunk)")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py measures one GPU: the library has no multi-GPU path (each GPU would run the same "
             "step on its own groups); run with --gpus 1")
         sys.exit(2)
+    cfg, variant = variant_config(args)
 
     import torch
     from kv_cache_token_amd import _lib
@@ -517,7 +559,7 @@ def main():
         return
     dev_name = torch.cuda.get_device_name(0)
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
-    wl = Workload(torch, args.workload, streams, args.split)
+    wl = Workload(torch, args.workload, streams, args.split, cfg)
     cfg = wl.cfg
     log("workload %s ready on %s: %d groups, %d calls per run" % (args.workload, dev_name, cfg.G, len(wl.blocks)))
 
@@ -560,7 +602,7 @@ def main():
     bytes_per_launch = sum(dom_bytes) / len(dom_bytes)
     achieved = bytes_per_launch / (mean_ms * 1e-3) / 1e9
     sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-    mt = MEASURED_TRAFFIC.get(args.workload)
+    mt = None if variant else MEASURED_TRAFFIC.get(args.workload)
     traffic = mt["bytes_per_launch"] if mt and sha == mt["kernel_src_sha256_16"] else None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic, "traffic_unit": "bytes/launch",
@@ -573,10 +615,10 @@ def main():
         "metric": "evicted-cache tokens/sec (score+select+compact), achieved HBM GB/s vs peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": cfg.dtype,
         "data": "synthetic (seeded, HBM-resident; keys %s, V ~ N(0,1))" % {
             "aniso": "drift*mu + N(0,0.25)", "lognorm": "r*u, ln r ~ N(0,0.25)", "gauss": "N(0,1)"}[cfg.keys],
-        "config": {"workload": DESCRIPTIONS[args.workload], "groups": cfg.G,
+        "config": {"workload": DESCRIPTIONS[args.workload] + ("; " + variant if variant else ""), "groups": cfg.G,
                    "tokens_per_step": wl.tokens_per_step, "runs_per_step": len(wl.plans),
                    "budget": cfg.budget, "streams": args.streams, "split": args.split, "graph": bool(graph),
                    "input_sets": len(wl.plan_sets), "device": dev_name},

@@ -4,7 +4,8 @@ This module only draws random K/V rows and filter directions.  It holds none of
 the eviction method's arithmetic (no scoring, ranking or compaction), so that the
 CPU oracle and the HIP path can both consume the very same bytes.
 
-Workloads (all head_dim D = 128, groups g = (l*B + b)*H + h):
+Workloads (head_dim D = 128 unless a variant sets ``Config.D``; groups
+g = (l*B + b)*H + h):
 
 * ``c1`` -- one layer, one KV head, fp32 K/V ~ N(0, 1); one 1024-token block,
   budget 512, 4 sinks, no recent window, L2 norm keep-low.
@@ -60,7 +61,7 @@ class Config:
     L: int
     B: int
     H: int
-    dtype: str                  # "f32" or "bf16"
+    dtype: str                  # "f32", "bf16" or "f16"
     keys: str                   # "gauss", "aniso", "lognorm"
     chunks: Tuple[int, ...]     # incoming rows per call, in order
     budget: int
@@ -69,6 +70,7 @@ class Config:
     scorers: Tuple[Scorer, ...]
     calib_tokens: int = 0
     calib_keys: str = "crossing"   # fallback estimate from the whole crossing block, or the "first" calib_tokens
+    D: int = 128                   # head dim (64, 128 or 256)
 
     @property
     def G(self) -> int:
@@ -141,13 +143,13 @@ def bits_to_f32(b: np.ndarray, dtype: str) -> np.ndarray:
 
 def planted_mu(cfg: Config, l: int, h: int) -> np.ndarray:
     """Unit direction mu_{l,h} (float64) planted in the anisotropic key recipe."""
-    m = _rng(cfg.cid, l, 0, h, 0, TAG_MU).standard_normal(D)
+    m = _rng(cfg.cid, l, 0, h, 0, TAG_MU).standard_normal(cfg.D)
     return m / np.linalg.norm(m)
 
 
 def filters_mu(cfg: Config) -> np.ndarray:
     """[L, H, D] float32 filters equal to the planted directions."""
-    out = np.empty((cfg.L, cfg.H, D), dtype=np.float32)
+    out = np.empty((cfg.L, cfg.H, cfg.D), dtype=np.float32)
     for l in range(cfg.L):
         for h in range(cfg.H):
             out[l, h] = planted_mu(cfg, l, h).astype(np.float32)
@@ -157,14 +159,14 @@ def filters_mu(cfg: Config) -> np.ndarray:
 def _keys_f32(cfg: Config, g: int, chunk: int, S: int) -> np.ndarray:
     l, b, h = cfg.group_lbh(g)
     if cfg.keys == "gauss":
-        return _rng(cfg.cid, l, b, h, chunk, TAG_K).standard_normal((S, D), dtype=np.float32)
+        return _rng(cfg.cid, l, b, h, chunk, TAG_K).standard_normal((S, cfg.D), dtype=np.float32)
     if cfg.keys == "aniso":
         mu = planted_mu(cfg, l, h)
         drift = _rng(cfg.cid, l, b, h, chunk, TAG_DRIFT).uniform(0.5, 2.0, S)
-        noise = _rng(cfg.cid, l, b, h, chunk, TAG_K).standard_normal((S, D), dtype=np.float32)
+        noise = _rng(cfg.cid, l, b, h, chunk, TAG_K).standard_normal((S, cfg.D), dtype=np.float32)
         return (drift[:, None] * mu[None, :] + 0.5 * noise.astype(np.float64)).astype(np.float32)
     if cfg.keys == "lognorm":
-        u = _rng(cfg.cid, l, b, h, chunk, TAG_K).standard_normal((S, D))
+        u = _rng(cfg.cid, l, b, h, chunk, TAG_K).standard_normal((S, cfg.D))
         u /= np.linalg.norm(u, axis=1, keepdims=True)
         r = np.exp(0.5 * _rng(cfg.cid, l, b, h, chunk, TAG_LOGNORM).standard_normal(S))
         return (r[:, None] * u).astype(np.float32)
@@ -173,7 +175,7 @@ def _keys_f32(cfg: Config, g: int, chunk: int, S: int) -> np.ndarray:
 
 def _values_f32(cfg: Config, g: int, chunk: int, S: int) -> np.ndarray:
     l, b, h = cfg.group_lbh(g)
-    return _rng(cfg.cid, l, b, h, chunk, TAG_V).standard_normal((S, D), dtype=np.float32)
+    return _rng(cfg.cid, l, b, h, chunk, TAG_V).standard_normal((S, cfg.D), dtype=np.float32)
 
 
 def encode(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -303,35 +305,37 @@ def query_acts_device(L: int, H_q: int, H_kv: int, N: int, D: int = 128, seed: i
 # ----------------------------------------------------------------------------
 
 def fill_device(cfg: Config, rows: int, seed: int, device="cuda", exact=None, mus=None):
-    """Return device tensors (K, V) of shape [G, rows, D] following ``cfg``'s
+    """Return device tensors (K, V) of shape [G, rows, cfg.D] following ``cfg``'s
     recipe with torch's seeded generator.  ``exact`` maps group -> host (K, V)
     [rows, D] arrays (from ``group_chunk`` / ``group_stream``) that overwrite
     those groups, so that they carry the exact bytes the oracle sees.
 
-    bf16 tensors are returned as torch.bfloat16, fp32 as torch.float32."""
+    bf16 tensors are returned as torch.bfloat16, f16 as torch.float16, fp32 as
+    torch.float32."""
     import torch
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
-    G = cfg.G
+    G, D_ = cfg.G, cfg.D
     if cfg.keys == "gauss":
-        k = torch.randn((G, rows, D), generator=gen, device=device, dtype=torch.float32)
+        k = torch.randn((G, rows, D_), generator=gen, device=device, dtype=torch.float32)
     elif cfg.keys == "aniso":
         if mus is None:
             mus = device_mus(cfg, device)
         drift = torch.rand((G, rows, 1), generator=gen, device=device) * 1.5 + 0.5
-        k = torch.randn((G, rows, D), generator=gen, device=device, dtype=torch.float32)
+        k = torch.randn((G, rows, D_), generator=gen, device=device, dtype=torch.float32)
         k.mul_(0.5).add_(drift * mus[:, None, :])
     elif cfg.keys == "lognorm":
-        k = torch.randn((G, rows, D), generator=gen, device=device, dtype=torch.float32)
+        k = torch.randn((G, rows, D_), generator=gen, device=device, dtype=torch.float32)
         k.div_(k.norm(dim=2, keepdim=True))
         r = torch.exp(0.5 * torch.randn((G, rows, 1), generator=gen, device=device))
         k.mul_(r)
     else:
         raise ValueError(cfg.keys)
-    v = torch.randn((G, rows, D), generator=gen, device=device, dtype=torch.float32)
-    if cfg.dtype == "bf16":
-        k = k.to(torch.bfloat16)
-        v = v.to(torch.bfloat16)
+    v = torch.randn((G, rows, D_), generator=gen, device=device, dtype=torch.float32)
+    if cfg.dtype in ("bf16", "f16"):
+        td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float16
+        k = k.to(td)
+        v = v.to(td)
     for g, (Kh, Vh) in (exact or {}).items():
         k[g].copy_(host_to_torch(Kh, cfg.dtype))
         v[g].copy_(host_to_torch(Vh, cfg.dtype))

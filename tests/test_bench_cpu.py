@@ -49,3 +49,24 @@ def test_measured_traffic_matches_the_committed_counter_summaries():
         assert abs(mt["bytes_per_launch"] - dom) <= 1, w
         trace = open(os.path.join(ROOT, "profiles", stem + "_kernel_stats.md")).read()
         assert "`%s`" % sha in trace, w
+
+
+def test_prefill_variants_resize_the_recipe_and_reach_the_oracle_leg():
+    import dataclasses
+    import bench
+    from kv_cache_token_amd import synth
+    ns = dict(workload="c4", dtype="f16", head_dim=64, budget=20000, chunk=16384, tokens=65536)
+    cfg, text = bench.variant_config(types.SimpleNamespace(**ns))
+    assert (cfg.dtype, cfg.D, cfg.budget, cfg.chunks) == ("f16", 64, 20000, (16384,) * 4)
+    assert cfg.scorers == synth.CONFIGS[4].scorers and "f16" in text and "20000" in text
+    same, text0 = bench.variant_config(types.SimpleNamespace(workload="c4", dtype=None, head_dim=None, budget=None,
+                                                             chunk=None, tokens=None))
+    assert same is synth.CONFIGS[4] and text0 == ""
+    for bad in (dict(ns, workload="c3"), dict(ns, tokens=1000), dict(ns, workload="c5", head_dim=256)):
+        with pytest.raises(SystemExit):
+            bench.variant_config(types.SimpleNamespace(**bad))
+    # the oracle leg runs the variant's own bytes (fp16 rows of 64 elements)
+    small = dataclasses.replace(cfg, chunks=(300,) * 3, budget=500)
+    wl = types.SimpleNamespace(cfg=small, tokens_per_step=2 * 900)
+    cb = bench.cpu_baseline(wl, 2, min_seconds=0.1)
+    assert cb["value"] > 0

@@ -43,7 +43,7 @@ def _run(cfg, scorer, sample, seed=1234, check_every=None):
     f_lh = synth.filters_mu(cfg) if scorer.filt == "mu" else None
     cache = EvictingCache(cfg.L, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, scorer.mode,
                           None if f_lh is None else torch.from_numpy(f_lh), scorer.sign, cfg.dtype,
-                          calib_tokens=cfg.calib_tokens, calib_keys=cfg.calib_keys)
+                          calib_tokens=cfg.calib_tokens, calib_keys=cfg.calib_keys, head_dim=cfg.D)
     f_s = None
     if f_lh is not None:
         f_s = np.stack([f_lh[cfg.group_lbh(g)[0], cfg.group_lbh(g)[2]] for g in sample])
@@ -75,20 +75,20 @@ def _run(cfg, scorer, sample, seed=1234, check_every=None):
         if lock is None:
             if scorer.filt == "keysvd":
                 # the oracle estimates its own filter from the same first keys
-                kw = synth.bf16_bits_to_f32(Kh[:, :cfg.calib_tokens]).astype(np.float64) \
-                    if cfg.dtype == "bf16" else Kh[:, :cfg.calib_tokens].astype(np.float64)
+                kw = synth.bits_to_f32(Kh[:, :cfg.calib_tokens], cfg.dtype).astype(np.float64)
                 f_s = np.stack([calib.estimate_filter_dir(kw[i]) for i in range(ns)]).astype(np.float32)
-                f_gpu = cache.filters.reshape(cfg.G, D).cpu().numpy()[sample]
+                f_gpu = cache.filters.reshape(cfg.G, cfg.D).cpu().numpy()[sample]
                 cos = np.sum(f_s.astype(np.float64) * f_gpu, axis=1)
                 assert np.all(cos > 1 - 1e-6), cos
-            lock = oracle.OracleCache(ns, D, cfg.dtype, cfg.budget, cfg.n_sink, cfg.recent, keep, scorer.mode,
+            lock = oracle.OracleCache(ns, cfg.D, cfg.dtype, cfg.budget, cfg.n_sink, cfg.recent, keep, scorer.mode,
                                       f_s, scorer.sign)
             ind = lock.copy()
         s_gpu = cache.last_scores()[sample].cpu().numpy()
         lock.update(Kh, Vh, scores_in=s_gpu)
         ind.update(Kh, Vh)
         for i, g in enumerate(sample):
-            s_ref_all[g].append(oracle.score(Kh[i], scorer.mode, None if f_s is None else f_s[i], scorer.sign))
+            s_ref_all[g].append(oracle.score(Kh[i], scorer.mode, None if f_s is None else f_s[i], scorer.sign,
+                                             dtype=cfg.dtype))
             scale_all[g].append(score_scale(Kh[i], cfg.dtype, scorer.mode, None if f_s is None else f_s[i]))
             s_gpu_all[g].append(s_gpu[i])
         tokens += S
@@ -173,3 +173,24 @@ def test_c4_chunked_prefill_32k(which):
 def test_c5_keysvd_fallback_128k():
     cfg = synth.CONFIGS[5]
     _run(cfg, cfg.scorers[0], synth.sample_groups(cfg, 6), check_every=4)
+
+
+# The prefill recipe at other sizes (the bench's variant options): fp16 and fp32
+# rows, head dims 64 and 256, and a budget whose calls select over more rows
+# than one workgroup holds (the multi-block selection on every evicting call
+# after the first).
+VARIANTS = [("f16", 64, 4096, 4096, 32768, 0), ("f32", 256, 4096, 4096, 32768, 1),
+            ("bf16", 128, 20000, 16384, 65536, 0), ("f16", 128, 20000, 16384, 65536, 1)]
+
+
+@pytest.mark.parametrize("dtype,Dd,budget,chunk,tokens,which", VARIANTS, ids=[str(v) for v in VARIANTS])
+def test_c4_variants_full_size(dtype, Dd, budget, chunk, tokens, which):
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS[4], dtype=dtype, D=Dd, budget=budget, chunks=(chunk,) * (tokens // chunk))
+    _run(cfg, cfg.scorers[which], synth.sample_groups(cfg, 6), check_every=1)
+
+
+def test_c5_fallback_fp16_head_dim_64():
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS[5], dtype="f16", D=64, chunks=(8192,) * 4)
+    _run(cfg, cfg.scorers[0], synth.sample_groups(cfg, 6), check_every=1)
