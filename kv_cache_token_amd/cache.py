@@ -17,7 +17,6 @@ import numpy as np
 
 from . import api
 
-D = api.D
 LAST_LEVEL_CACHE_BYTES = 256 << 20   # MI355X's last-level (Infinity) cache
 
 
