@@ -270,26 +270,33 @@ __device__ __forceinline__ void count_digits(const uint32_t *key, int r0, int n_
 
 // One wave: lane l holds the counts of bins 255-4l (c.w) down to 252-4l (c.x).
 // Finds the bin where the krem-th largest key falls; the owning lane returns
-// true and sets the digit and the remaining rank inside that bin.
-__device__ __forceinline__ bool pick_digit(uint4 c, uint32_t krem, uint32_t *digit, uint32_t *nk) {
+// true and sets the digit, the remaining rank inside that bin and, if asked,
+// whether that rank is the bin's last (every key of the bin is kept).
+__device__ __forceinline__ bool pick_digit(uint4 c, uint32_t krem, uint32_t *digit, uint32_t *nk,
+                                           uint32_t *whole = nullptr) {
     const int lane = threadIdx.x & 63;
     const uint32_t c0 = c.w, c1 = c.z, c2 = c.y, c3 = c.x;
     const uint32_t local = c0 + c1 + c2 + c3;
     const uint32_t incl = wave_prefix_incl(local);  // keys in this lane's bins or higher ones
     const uint32_t above = incl - local;
     if (!(above < krem && krem <= incl)) return false;
-    uint32_t cum = above;
+    uint32_t cum = above, cnt;
     if (cum + c0 >= krem) {
         *digit = 255 - 4 * lane;
+        cnt = c0;
     } else if ((cum += c0) + c1 >= krem) {
         *digit = 254 - 4 * lane;
+        cnt = c1;
     } else if ((cum += c1) + c2 >= krem) {
         *digit = 253 - 4 * lane;
+        cnt = c2;
     } else {
         cum += c2;
         *digit = 252 - 4 * lane;
+        cnt = c3;
     }
     *nk = krem - cum;
+    if (whole) *whole = *nk == cnt;
     return true;
 }
 
@@ -380,7 +387,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
                        keep_low};
 
     __shared__ uint4 hist4[2][64];  // 256-bin histograms, two passes' worth
-    __shared__ uint32_t sel[2];
+    __shared__ uint32_t sel[3];
     __shared__ uint32_t chunk[M * NW];
     uint32_t(*hist)[256] = reinterpret_cast<uint32_t(*)[256]>(hist4);
 
@@ -389,7 +396,13 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
     if (t < 64) hist4[0][t] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
+    // After the four passes the prefix is the whole key: tau = prefix and
+    // quota = krem.  A pass whose chosen bin is kept whole ends the passes
+    // early: the kept rows are then exactly the keys >= the prefix, i.e. tau =
+    // prefix - 1 with no quota.
     uint32_t prefix = 0, pmask = 0, krem = (uint32_t)budget;
+    uint32_t tau = 0, quota = 0;
+    bool whole = false;
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
@@ -397,10 +410,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
         __syncthreads();
         if (w == 0) {
             const uint4 c = hist4[pass & 1][63 - t];
-            uint32_t d, nk;
-            if (pick_digit(c, krem, &d, &nk)) {
+            uint32_t d, nk, all;
+            if (pick_digit(c, krem, &d, &nk, &all)) {
                 sel[0] = d;
                 sel[1] = nk;
+                sel[2] = all;
             }
         }
         if (pass < 3 && w == 1)  // wave 1 clears the next pass's histogram meanwhile
@@ -409,8 +423,19 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
         prefix |= sel[0] << shift;
         pmask |= 0xFFu << shift;
         krem = sel[1];
+        if (pass < 3 && sel[2] && prefix != 0) {  // the same in every thread
+            whole = true;
+            break;
+        }
     }
-    write_kept<M, NT>(key, 0, n_total, prefix, krem, 0, 0, out, budget, chunk);
+    if (whole) {
+        tau = prefix - 1;
+        quota = 0;
+    } else {
+        tau = prefix;
+        quota = krem;
+    }
+    write_kept<M, NT>(key, 0, n_total, tau, quota, 0, 0, out, budget, chunk);
 }
 
 // --- multi-block selection (n_total above the on-chip bound) --------------
