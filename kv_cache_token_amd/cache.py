@@ -242,6 +242,14 @@ class EvictingCache:
         """Absorb one block: k_new, v_new [G, S, D] (or [L, B, H, S, D])."""
         self._step(k_new, v_new, prepare=False)
 
+    def update_and_fetch(self, k_new, v_new):
+        """The pages' per-block call (Q-Filters page, "Usage"): absorb the block
+        and return the kept rows' (K, V) views [G, n, D] in temporal order;
+        `offset` is then the true position of the next token."""
+        self.update(k_new, v_new)
+        k, v, _, _ = self.kept()
+        return k, v
+
     def _step(self, k_new, v_new, prepare: bool):
         S = k_new.shape[-2]
         k_new = k_new.contiguous().reshape(self.G, S, self.D)

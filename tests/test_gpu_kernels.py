@@ -433,6 +433,27 @@ def test_runs_are_deterministic():
             assert torch.equal(a, b)
 
 
+def test_update_and_fetch_returns_the_kept_rows_and_true_offset():
+    """The pages' per-block call: kept (K, V) in temporal order, the offset the
+    true token count (200 then 120 tokens at budget 64)."""
+    import torch
+    from kv_cache_token_amd.cache import EvictingCache
+    G = 3
+    c = EvictingCache(1, 1, G, 64, 4, 0, "low", "l2")
+    o = oracle.OracleCache(G, D, "bf16", 64, 4, 0, "low")
+    for blk, S in enumerate((200, 120)):
+        K = synth.custom_keys((G, S, D), 60 + blk, "bf16")
+        V = synth.custom_keys((G, S, D), 70 + blk, "bf16")
+        k, v = c.update_and_fetch(_t(K, "bf16"), _t(V, "bf16"))
+        o.update(K, V, scores_in=c.last_scores().cpu().numpy())
+    torch.cuda.synchronize()
+    assert c.offset == 320 and k.shape == (G, 64, D) and v.shape == (G, 64, D)
+    for g in range(G):
+        ok, ov, _, _ = o.kept(g)
+        assert np.array_equal(synth.torch_to_host(k[g], "bf16"), ok)
+        assert np.array_equal(synth.torch_to_host(v[g], "bf16"), ov)
+
+
 @pytest.mark.parametrize("mode,sign", [("l2", 1), ("proj", -1)])
 def test_score_cache_hint_changes_nothing_but_the_loads(mode, sign):
     """mode | KVX_SCORE_CACHE_KEYS gives the same scores bit for bit, on the
