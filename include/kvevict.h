@@ -226,8 +226,11 @@ KVX_API int kv_evict_one_inplace(void *k_cache, void *v_cache, float *s_cache,
  *   L, H_kv, D       the layout the caller's model has
  *   out              host [L, H_kv, D] float32
  *   n_samples_out    optional (may be NULL)
- * Errors: KVX_EIO (missing file, bad zip/npy, missing field, wrong dtype),
- * KVX_EMISMATCH (version, model id, layer count, head layout or D differ).
+ * Every member's CRC-32 is checked, and offsets and sizes that point outside
+ * the file are refused before anything is read through them.
+ * Errors: KVX_EIO (missing file, bad zip/npy, checksum mismatch, missing field,
+ * wrong dtype), KVX_EMISMATCH (version, model id, layer count, head layout or
+ * D differ).
  */
 KVX_API int qf_filters_load(const char *path, const char *expect_model_id, int64_t L,
                             int64_t H_kv, int64_t D, float *out, int64_t *n_samples_out);

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <array>
 #include <string>
 #include <thread>
 #include <vector>
@@ -230,7 +231,29 @@ bool parse_npy(const std::string &blob, NpyArray *a) {
     return true;
 }
 
-// Reads every stored member of a ZIP archive through its central directory.
+// CRC-32 of the ZIP format (reflected polynomial 0xEDB88320).  The table is a
+// function-local static, so its one-time initialisation is thread-safe.
+uint32_t crc32_of(const unsigned char *d, size_t n) {
+    static const std::array<uint32_t, 256> table = [] {
+        std::array<uint32_t, 256> t{};
+        for (uint32_t i = 0; i < 256; ++i) {
+            uint32_t c = i;
+            for (int k = 0; k < 8; ++k) c = (c & 1) ? 0xEDB88320u ^ (c >> 1) : c >> 1;
+            t[i] = c;
+        }
+        return t;
+    }();
+    uint32_t c = 0xFFFFFFFFu;
+    for (size_t i = 0; i < n; ++i) c = table[(c ^ d[i]) & 0xFF] ^ (c >> 8);
+    return c ^ 0xFFFFFFFFu;
+}
+uint32_t crc32_of(const std::string &d) { return crc32_of((const unsigned char *)d.data(), d.size()); }
+
+// Whether [off, off + len) lies inside a buffer of `size` bytes (no overflow).
+inline bool in_file(uint64_t off, uint64_t len, uint64_t size) { return off <= size && len <= size - off; }
+
+// Reads every stored member of a ZIP archive through its central directory,
+// checking each member's CRC-32.
 int read_zip(const char *path, std::vector<std::pair<std::string, std::string>> *members) {
     FILE *f = fopen(path, "rb");
     if (!f) return set_error(KVX_EIO, "cannot open '%s'", path);
@@ -254,35 +277,42 @@ int read_zip(const char *path, std::vector<std::pair<std::string, std::string>> 
     if (cd_off == 0xFFFFFFFFu || count == 0xFFFFu) {  // ZIP64 end record via its locator
         if (eocd < 20 || rd32(b + eocd - 20) != 0x07064b50u) return set_error(KVX_EIO, "'%s': bad zip64 locator", path);
         const uint64_t z = rd64(b + eocd - 20 + 8);
-        if (z + 56 > size || rd32(b + z) != 0x06064b50u) return set_error(KVX_EIO, "'%s': bad zip64 end record", path);
+        if (!in_file(z, 56, size) || rd32(b + z) != 0x06064b50u)
+            return set_error(KVX_EIO, "'%s': bad zip64 end record", path);
         count = rd64(b + z + 32);
         cd_off = rd64(b + z + 48);
     }
     size_t p = cd_off;
     for (uint64_t e = 0; e < count; ++e) {
-        if (p + 46 > size || rd32(b + p) != 0x02014b50u) return set_error(KVX_EIO, "'%s': bad central directory", path);
+        if (!in_file(p, 46, size) || rd32(b + p) != 0x02014b50u)
+            return set_error(KVX_EIO, "'%s': bad central directory", path);
         const uint16_t method = rd16(b + p + 10);
+        const uint32_t crc = rd32(b + p + 16);
         uint64_t csize = rd32(b + p + 20), usize = rd32(b + p + 24);
         const uint16_t nlen = rd16(b + p + 28), xlen = rd16(b + p + 30), clen = rd16(b + p + 32);
         uint64_t lho = rd32(b + p + 42);
-        if (p + 46 + nlen + xlen > size) return set_error(KVX_EIO, "'%s': truncated entry", path);
+        if (!in_file(p + 46, (uint64_t)nlen + xlen, size)) return set_error(KVX_EIO, "'%s': truncated entry", path);
         std::string name((const char *)b + p + 46, nlen);
         const unsigned char *x = b + p + 46 + nlen, *xe = x + xlen;
-        while (x + 4 <= xe) {  // ZIP64 extra: the fields that overflowed, in this order
+        while (xe - x >= 4) {  // ZIP64 extra: the fields that overflowed, in this order
             const uint16_t id = rd16(x), sz = rd16(x + 2);
-            const unsigned char *d = x + 4;
+            if (sz > xe - x - 4) break;  // a field running past the extra block
+            const unsigned char *d = x + 4, *fe = x + 4 + sz;
             if (id == 0x0001) {
-                if (usize == 0xFFFFFFFFu && d + 8 <= x + 4 + sz) usize = rd64(d), d += 8;
-                if (csize == 0xFFFFFFFFu && d + 8 <= x + 4 + sz) csize = rd64(d), d += 8;
-                if (lho == 0xFFFFFFFFu && d + 8 <= x + 4 + sz) lho = rd64(d), d += 8;
+                if (usize == 0xFFFFFFFFu && fe - d >= 8) usize = rd64(d), d += 8;
+                if (csize == 0xFFFFFFFFu && fe - d >= 8) csize = rd64(d), d += 8;
+                if (lho == 0xFFFFFFFFu && fe - d >= 8) lho = rd64(d), d += 8;
             }
-            x += 4 + sz;
+            x = fe;
         }
         if (method != 0) return set_error(KVX_EIO, "'%s': member '%s' is compressed (only stored members are read)", path, name.c_str());
         if (csize != usize) return set_error(KVX_EIO, "'%s': member '%s' has inconsistent sizes", path, name.c_str());
-        if (lho + 30 > size || rd32(b + lho) != 0x04034b50u) return set_error(KVX_EIO, "'%s': bad local header", path);
+        if (!in_file(lho, 30, size) || rd32(b + lho) != 0x04034b50u)
+            return set_error(KVX_EIO, "'%s': bad local header", path);
         const uint64_t data = lho + 30 + rd16(b + lho + 26) + rd16(b + lho + 28);
-        if (data + csize > size) return set_error(KVX_EIO, "'%s': member '%s' is truncated", path, name.c_str());
+        if (!in_file(data, csize, size)) return set_error(KVX_EIO, "'%s': member '%s' is truncated", path, name.c_str());
+        if (crc32_of(b + data, csize) != crc)
+            return set_error(KVX_EIO, "'%s': member '%s' fails its CRC-32 check", path, name.c_str());
         members->emplace_back(name, buf.substr(data, csize));
         p += 46 + nlen + xlen + clen;
     }
@@ -342,21 +372,7 @@ bool npy_int64(const NpyArray &a, int64_t *out) {
     return false;
 }
 
-uint32_t crc32_of(const std::string &d) {
-    static uint32_t table[256];
-    static bool init = false;
-    if (!init) {
-        for (uint32_t i = 0; i < 256; ++i) {
-            uint32_t c = i;
-            for (int k = 0; k < 8; ++k) c = (c & 1) ? 0xEDB88320u ^ (c >> 1) : c >> 1;
-            table[i] = c;
-        }
-        init = true;
-    }
-    uint32_t c = 0xFFFFFFFFu;
-    for (unsigned char ch : d) c = table[(c ^ ch) & 0xFF] ^ (c >> 8);
-    return c ^ 0xFFFFFFFFu;
-}
+
 
 std::string npy_blob(const std::string &descr, const std::vector<int64_t> &shape, const std::string &data) {
     std::string shp = "(";

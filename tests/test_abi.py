@@ -154,6 +154,45 @@ def test_artifact_round_trip_and_mismatches(tmp_path):
     assert zipfile.is_zipfile(p2)
 
 
+def test_corrupt_artifacts_are_rejected(tmp_path):
+    """A flipped byte in a member fails its CRC-32; offsets and sizes that point
+    past the file (including ones that would wrap 64-bit arithmetic) and
+    truncations are refused, never read."""
+    import struct
+    f = np.random.default_rng(2).standard_normal((3, 2, D)).astype(np.float32)
+    good = str(tmp_path / "good.npz")
+    api.qf_filters_save(good, f, "m", 1, "d")
+    raw = bytearray(open(good, "rb").read())
+    pos = raw.find(f.tobytes()[:16])
+    assert pos > 0
+    cases = {}
+    flipped = bytearray(raw)
+    flipped[pos + 100] ^= 0x01
+    cases["flipped"] = flipped
+    cases["truncated"] = raw[: len(raw) // 2]
+    eocd = raw.rfind(b"PK\x05\x06")
+    cd_off = struct.unpack_from("<I", raw, eocd + 16)[0]
+    for name, field, value in (("cd_offset", eocd + 16, 0xFFFFFFF0), ("local_offset", cd_off + 42, 0xFFFFFFF0),
+                               ("size", cd_off + 20, 0xFFFFFFF0)):
+        b = bytearray(raw)
+        struct.pack_into("<I", b, field, value)
+        if name == "size":
+            struct.pack_into("<I", b, cd_off + 24, value)
+        cases[name] = b
+    # a zip64 end record whose central directory offset wraps around 2^64
+    b = bytearray(raw)
+    struct.pack_into("<I", b, eocd + 16, 0xFFFFFFFF)
+    loc = struct.pack("<IIQI", 0x07064B50, 0, eocd, 1)   # the zip64 record sits where the end record was
+    z64 = struct.pack("<IQHHIIQQQQ", 0x06064B50, 44, 45, 45, 0, 0, 5, 5, 100, 2 ** 64 - 8)
+    cases["zip64_wrap"] = bytes(b[:eocd]) + z64 + loc + bytes(b[eocd:])
+    for name, data in cases.items():
+        p = str(tmp_path / (name + ".npz"))
+        open(p, "wb").write(bytes(data))
+        with pytest.raises(KvxError) as e:
+            api.qf_filters_load(p, 3, 2)
+        assert e.value.code == _lib.KVX_EIO, name
+
+
 def test_query_filters_match_oracle():
     rng = np.random.default_rng(1)
     Hq, N, Hkv = 24, 600, 8
