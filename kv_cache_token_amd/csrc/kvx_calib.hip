@@ -120,7 +120,8 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
     static_assert(SLOTS >= 1 && NT % R::kLanes == 0, "a workgroup covers whole rows");
     static_assert(SLOTS <= CH, "the column partial sums fit the staging buffer");
     __shared__ double xd[CH * S];  // staged rows, or C while it is squared; first the column partial sums
-    __shared__ double cs[HD], mu[HD], v[HD], y[HD], w[HD], acc[HD], yp[L::QW][HD], lam[2], red[NT / 64];
+    __shared__ double cs[HD], mu[HD], v[HD], y[HD], w[HD], acc[HD], yp[L::QW][HD], lam[2], red[NT / 64],
+        fr[NT / 64];
     __shared__ int flag;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int lr = lane & 15, lk = lane >> 4;
@@ -377,28 +378,60 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
             }
         }
         int st = f == 2 ? 2 : (calm >= 2 ? 0 : 1);
+        double fro_all = 0.0;  // |C|_F^2 of the current C, summed over the workgroup
         if (st == 0) {
-            // Separation check: lambda1 is the Rayleigh quotient of v; lambda2 is
-            // approached from below by power iteration on the complement of v
-            // (w kept orthogonal to v), for at most kSepSteps steps.  Equal top
-            // eigenvalues (lambda2 >= lambda1 (1 - 1e-9)) are reported as status
-            // 1; on the p-th power of C that is a ratio of 1 - p 1e-9.  A tie
-            // whose eigenvalues stand clear of the rest shows within a few steps;
-            // top eigenvalues that are close but not tied have already kept the
-            // main iteration from converging.
-            matvec(v);
-            if (t < 64) {
-                gather_y();
-                const double l1 = wdot(v, y);
-                if (lane == 0) lam[0] = l1;
+            // Separation check: equal top eigenvalues (lambda2 >= lambda1 (1 -
+            // 1e-9)) are reported as status 1; on the p-th power of C that is a
+            // ratio of 1 - p 1e-9.  lambda1 is the Rayleigh quotient of v.  C is a
+            // Gram matrix (symmetric, positive semi-definite), so lambda2^2 <=
+            // sum_{i>=2} lambda_i^2 = |C|_F^2 - lambda1^2: when that is below
+            // the tie threshold the separation is certified at once.  If not,
+            // and the same bound on C^2 can still pass (by Cauchy-Schwarz it
+            // cannot once (sum_{i>=2} lambda_i^2)^2 / (D - 1) reaches lambda1^4),
+            // C is squared and the bound tried again.  Otherwise lambda2 is
+            // approached from below by power iteration on the complement of v (w
+            // kept orthogonal to v), for at most kSepSteps steps: a tie whose
+            // eigenvalues stand clear of the rest shows within a few steps; top
+            // eigenvalues that are close but not tied have already kept the main
+            // iteration from converging.
+            bool certified = false;
+            for (int round = 0; round < 2 && !certified; ++round) {
+                if (round == 1) {
+                    const double l1 = lam[0], rest = fro_all - l1 * l1;
+                    const double lim2 = l1 * l1 * (1.0 - 2e-9 * power);
+                    if (!(rest * rest < (double)(HD - 1) * lim2 * lim2)) break;  // C^2 cannot pass either
+                    square();
+                    power *= 2.0;
+                }
+                matvec(v);
+                if (t < 64) {
+                    gather_y();
+                    const double l1 = wdot(v, y);
+                    if (lane == 0) lam[0] = l1;
+                }
+                double fro = 0.0;  // this lane's part of |C|_F^2
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq) fro = __builtin_fma(Cm[a][b][qq], Cm[a][b][qq], fro);
+                fro = wsum(fro);
+                if (lane == 0) fr[wv] = fro;
+                __syncthreads();
+                fro_all = 0.0;
+                for (int i = 0; i < NT / 64; ++i) fro_all += fr[i];
+                const double l1 = lam[0], lim = l1 * (1.0 - 1e-9 * power);
+                certified = l1 > 0.0 && fro_all - l1 * l1 < lim * lim;
+                __syncthreads();  // fr and lam are read before they are written again
             }
             start(w, 0x9E3779B9u);
             __syncthreads();
-            if (t < 64) renorm(w, w, v);  // orthogonalise and normalise the start
+            if (t < 64 && !certified) renorm(w, w, v);  // orthogonalise and normalise the start
             __syncthreads();
             int calm2 = 0;
             constexpr int kSepSteps = 48;
-            for (int it2 = 0; it2 < kSepSteps; ++it2) {
+            for (int it2 = 0; it2 < (certified ? 0 : kSepSteps); ++it2) {
                 matvec(w);
                 if (t < 64) {
                     gather_y();
