@@ -79,13 +79,17 @@ __global__ __launch_bounds__(256) void append_rows_kernel(const char *__restrict
 
 enum { DIR_CENTRED_KEYS = 0, DIR_RAW_QUERIES = 1 };
 
+#ifndef KVX_SQUARE_EVERY
+#define KVX_SQUARE_EVERY 8
+#endif
+
 template <int HD>
 struct DirLayout {
     static constexpr int QW = HD / 64;     // quadrants of C per side
     static constexpr int NT = 64 * QW * QW;  // one wave per quadrant: 64 threads for HD 64, 256 for HD 128
     static constexpr int CH = HD;          // staged rows per chunk: an HD x HD fp64 square of LDS
     static constexpr int S = HD + 1;       // LDS row stride in doubles (column reads hit distinct banks)
-    static constexpr int SQUARE_EVERY = 32;  // power steps between squarings of C
+    static constexpr int SQUARE_EVERY = KVX_SQUARE_EVERY;  // power steps between squarings of C
     static constexpr int MAX_SQUARINGS = 10;
     static_assert(QW == 1 || QW == 2, "the device estimator covers head dims 64 and 128");
 };
