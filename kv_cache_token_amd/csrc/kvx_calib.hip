@@ -321,7 +321,11 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
 #pragma unroll
             for (int u = 0; u < kPer; ++u) {
                 const int rr = (t + u * NT) / R::kLanes;
-                if (rr >= rows) break;
+                if (rr >= rows) {  // past the chunk's end: zeros, so that steps need no bound checks
+#pragma unroll
+                    for (int k = 0; k < E; ++k) xd[rr * S + part * E + k] = 0.0;
+                    continue;
+                }
                 float f[E];
                 widen<DT>(raw[u], f);
 #pragma unroll
@@ -337,19 +341,30 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
             }
             if (base + CH < n) fetch(base + CH);
             __syncthreads();
-            for (int k0 = 0; k0 < rows; k0 += 4) {
-                // rows past the chunk's end count as zeros (k < CH since CH % 4 == 0)
-                const int k = k0 + lk;
-                const bool in = k < rows;
-                double av[4], bv[4];
+            // steps of four rows (the last one padded with the zero rows); the
+            // operands of the next step are read from LDS before this step's
+            // products are issued, so the matrix cores do not wait for them
+            const int steps = (rows + 3) >> 2;
+            double av[4], bv[4], an[4], bn[4];
+            auto operands = [&](int s, double *a_, double *b_) {
+                const int k = 4 * s + lk;
 #pragma unroll
-                for (int a = 0; a < 4; ++a) av[a] = in ? xd[k * S + R0 + 16 * a + lr] : 0.0;
+                for (int a = 0; a < 4; ++a) a_[a] = xd[k * S + R0 + 16 * a + lr];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) bv[b] = in ? xd[k * S + C0 + 16 * b + lr] : 0.0;
+                for (int b = 0; b < 4; ++b) b_[b] = xd[k * S + C0 + 16 * b + lr];
+            };
+            operands(0, av, bv);
+            for (int s = 0; s < steps; ++s) {
+                if (s + 1 < steps) operands(s + 1, an, bn);
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
 #pragma unroll
                     for (int b = 0; b < 4; ++b) Cm[a][b] = mfma16x16x4(av[a], bv[b], Cm[a][b]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    av[i] = an[i];
+                    bv[i] = bn[i];
+                }
             }
         }
         if constexpr (MODE == DIR_RAW_QUERIES) reduce_sums();  // begins with a barrier
