@@ -345,7 +345,7 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
             // operands of the next step are read from LDS before this step's
             // products are issued, so the matrix cores do not wait for them
             const int steps = (rows + 3) >> 2;
-            double av[4], bv[4], an[4], bn[4];
+            double a0[4], b0[4], a1[4], b1[4];  // two operand sets, used in turn
             auto operands = [&](int s, double *a_, double *b_) {
                 const int k = 4 * s + lk;
 #pragma unroll
@@ -353,19 +353,21 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
 #pragma unroll
                 for (int b = 0; b < 4; ++b) b_[b] = xd[k * S + C0 + 16 * b + lr];
             };
-            operands(0, av, bv);
-            for (int s = 0; s < steps; ++s) {
-                if (s + 1 < steps) operands(s + 1, an, bn);
+            auto products = [&](const double *a_, const double *b_) {
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) Cm[a][b] = mfma16x16x4(av[a], bv[b], Cm[a][b]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    av[i] = an[i];
-                    bv[i] = bn[i];
-                }
+                    for (int b = 0; b < 4; ++b) Cm[a][b] = mfma16x16x4(a_[a], b_[b], Cm[a][b]);
+            };
+            operands(0, a0, b0);
+            int s = 0;
+            for (; s + 1 < steps; s += 2) {
+                operands(s + 1, a1, b1);
+                products(a0, b0);
+                if (s + 2 < steps) operands(s + 2, a0, b0);
+                products(a1, b1);
             }
+            if (s < steps) products(a0, b0);
         }
         if constexpr (MODE == DIR_RAW_QUERIES) reduce_sums();  // begins with a barrier
         __syncthreads();
