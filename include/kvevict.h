@@ -79,7 +79,7 @@ extern "C" {
 #define KVX_HEAD_DIM 128     /* the head dim of every workload here; D may also be 64 or 256 */
 #define KVX_MAX_BUDGET (1 << 21)   /* largest budget accepted                          */
 #define KVX_MAX_TOTAL (1 << 22)    /* largest n_kept + S that one selection handles     */
-#define KVX_ONCHIP_TOTAL 32768     /* up to this n_total the selection needs no workspace */
+#define KVX_ONCHIP_TOTAL 262144    /* up to this n_total the selection needs no workspace */
 
 typedef struct {
     int64_t L, B, H; /* layers, batch, KV heads: G = L*B*H groups            */
@@ -139,7 +139,8 @@ KVX_API int qf_score_keys(const void *k_new, kvx_shape shape, int64_t S, int32_t
 /*
  * kv_evict_workspace_size -- bytes of device workspace kv_evict_topk needs for
  * these sizes: 0 when n_kept + S <= KVX_ONCHIP_TOTAL (one workgroup per group
- * selects on chip) or when nothing is evicted; otherwise
+ * selects: up to 32768 rows with every key in registers, beyond that reading
+ * the scores again at each radix pass) or when nothing is evicted; otherwise
  * G * (260 + 2 * ceil(n_total / 16384)) * 4 bytes for the multi-block
  * selection's histograms, state and block counts.  The caller allocates it;
  * kv_evict_topk initialises it itself on the stream (no memset needed), and

@@ -16,7 +16,7 @@ KVX_OK, KVX_EINVAL, KVX_ERANGE, KVX_EDEVICE, KVX_EIO, KVX_EMISMATCH = 0, -1, -2,
 KVX_F32, KVX_BF16, KVX_F16 = 0, 1, 2
 KVX_SCORE_L2, KVX_SCORE_PROJ, KVX_SCORE_CACHE_KEYS = 0, 1, 0x100
 KVX_KEEP_HIGH, KVX_KEEP_LOW = 0, 1
-KVX_HEAD_DIM, KVX_MAX_BUDGET, KVX_MAX_TOTAL, KVX_ONCHIP_TOTAL = 128, 1 << 21, 1 << 22, 32768
+KVX_HEAD_DIM, KVX_MAX_BUDGET, KVX_MAX_TOTAL, KVX_ONCHIP_TOTAL = 128, 1 << 21, 1 << 22, 1 << 18
 
 _CODES = {KVX_EINVAL: "EINVAL", KVX_ERANGE: "ERANGE", KVX_EDEVICE: "EDEVICE", KVX_EIO: "EIO",
           KVX_EMISMATCH: "EMISMATCH"}

@@ -195,9 +195,12 @@ __device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t v) {
 // (in row order) with key == tau, and their indices are written in row order
 // from per-64-row chunk counts.
 //
-// Up to KVX_ONCHIP_TOTAL rows one workgroup per group does everything on chip.
-// Beyond that, a group's rows are split over blocks of MB_ROWS rows and the
-// passes meet in a small device workspace (histogram, state, block counts).
+// Up to 32 * 1024 rows one workgroup per group holds every key in registers
+// (select_kernel); up to KVX_ONCHIP_TOTAL rows one workgroup per group streams
+// the keys from memory in chunks at every pass (select_stream_kernel; the
+// scores stay in the caches between passes).  Beyond that, a group's rows are
+// split over blocks of MB_ROWS rows and the passes meet in a small device
+// workspace (histogram, state, block counts).
 // ---------------------------------------------------------------------------
 struct SelRows {
     const float *sk;  // stored scores of the group's kept rows
@@ -210,19 +213,27 @@ struct SelRows {
 // end read the last row instead, and the source array is picked by address,
 // so no branch separates the loads.
 template <int M, int NT>
-__device__ __forceinline__ void load_keys(const SelRows &a, int r0, uint32_t *key) {
-    float s[M];
+__device__ __forceinline__ void load_scores(const SelRows &a, int r0, float *s) {
 #pragma unroll
     for (int i = 0; i < M; ++i) {
         const int r = min(r0 + i * NT + (int)threadIdx.x, a.n_total - 1);
         s[i] = *(r < a.n_kept ? a.sk + r : a.sn + (r - a.n_kept));
     }
+}
+template <int M, int NT>
+__device__ __forceinline__ void make_keys(const SelRows &a, int r0, const float *s, uint32_t *key) {
 #pragma unroll
     for (int i = 0; i < M; ++i) {
         const int r = r0 + i * NT + (int)threadIdx.x;
         const bool prot = r < a.n_sink || r >= a.n_total - a.recent;
         key[i] = r < a.n_total ? (prot ? 0xFFFFFFFFu : select_key(s[i], a.keep_low)) : 0u;
     }
+}
+template <int M, int NT>
+__device__ __forceinline__ void load_keys(const SelRows &a, int r0, uint32_t *key) {
+    float s[M];
+    load_scores<M, NT>(a, r0, s);
+    make_keys<M, NT>(a, r0, s, key);
 }
 
 // Count the digit (key >> shift) & 255 of every key that matches the prefix
@@ -311,7 +322,7 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 template <int M, int NT>
 __device__ __forceinline__ void write_kept(const uint32_t *key, int r0, int n_total, uint32_t tau, uint32_t quota,
                                            uint32_t base_gt, uint32_t base_eq, int32_t *out, int budget,
-                                           uint32_t *chunk) {
+                                           uint32_t *chunk, uint32_t *total = nullptr) {
     constexpr int NW = NT / 64, NCH = M * NW, CPL = (NCH + 63) / 64;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
 #pragma unroll
@@ -339,6 +350,7 @@ __device__ __forceinline__ void write_kept(const uint32_t *key, int r0, int n_to
             if (c < NCH) chunk[c] = run;
             run += a[j];
         }
+        if (total && lane == 63) *total = run;  // (#gt << 16) | #eq over all M * NT rows
     }
     __syncthreads();
 #pragma unroll
@@ -436,6 +448,96 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
         quota = krem;
     }
     write_kept<M, NT>(key, 0, n_total, tau, quota, 0, 0, out, budget, chunk);
+}
+
+// One workgroup of NT threads per group for n_total up to KVX_ONCHIP_TOTAL:
+// every pass streams the group's keys in chunks of MS * NT rows through
+// registers (the same counting, picking and early end as select_kernel), and
+// the kept rows are written chunk by chunk in row order, each chunk's slots
+// offset by the counts of the chunks before it.  Two score buffers are used
+// in turn, so that a chunk's loads are in flight while the one before it is
+// counted or written.
+template <int MS, int NT>
+__global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restrict__ s_kept,
+                                                             const float *__restrict__ s_new, int n_kept,
+                                                             int S, int budget, int n_sink, int recent,
+                                                             int keep_low, int32_t *__restrict__ keep_idx) {
+    constexpr int NW = NT / 64, CHUNK = MS * NT;
+    static_assert(NW >= 2, "wave 1 clears the histograms while wave 0 scans");
+    static_assert(CHUNK < 65536, "per-chunk counts are packed in 16 bits");
+    const int g = blockIdx.x;
+    const int t = threadIdx.x, w = t >> 6;
+    const int n_total = n_kept + S;
+    int32_t *out = keep_idx + (size_t)g * budget;
+    if (n_total <= budget) {
+        for (int r = t; r < n_total; r += NT) out[r] = r;
+        return;
+    }
+    const SelRows rows{s_kept + (size_t)g * budget, s_new + (size_t)g * S, n_kept, n_total, n_sink, recent,
+                       keep_low};
+    __shared__ uint4 hist4[2][64];
+    __shared__ uint32_t sel[3], tot;
+    __shared__ uint32_t chunk[MS * NW];
+    uint32_t(*hist)[256] = reinterpret_cast<uint32_t(*)[256]>(hist4);
+    if (t < 64) hist4[0][t] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    uint32_t prefix = 0, pmask = 0, krem = (uint32_t)budget;
+    bool whole = false;
+    uint32_t key[MS];
+    float sa[MS], sb[MS];
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        load_scores<MS, NT>(rows, 0, sa);
+        for (int r0 = 0; r0 < n_total; r0 += 2 * CHUNK) {
+            make_keys<MS, NT>(rows, r0, sa, key);
+            if (r0 + CHUNK < n_total) load_scores<MS, NT>(rows, r0 + CHUNK, sb);
+            count_digits<MS, NT>(key, r0, n_total, prefix, pmask, shift, hist[pass & 1]);
+            if (r0 + CHUNK >= n_total) break;
+            make_keys<MS, NT>(rows, r0 + CHUNK, sb, key);
+            if (r0 + 2 * CHUNK < n_total) load_scores<MS, NT>(rows, r0 + 2 * CHUNK, sa);
+            count_digits<MS, NT>(key, r0 + CHUNK, n_total, prefix, pmask, shift, hist[pass & 1]);
+        }
+        __syncthreads();
+        if (w == 0) {
+            const uint4 c = hist4[pass & 1][63 - t];
+            uint32_t d, nk, all;
+            if (pick_digit(c, krem, &d, &nk, &all)) {
+                sel[0] = d;
+                sel[1] = nk;
+                sel[2] = all;
+            }
+        }
+        if (pass < 3 && w == 1) hist4[(pass + 1) & 1][t - 64] = make_uint4(0, 0, 0, 0);
+        __syncthreads();
+        prefix |= sel[0] << shift;
+        pmask |= 0xFFu << shift;
+        krem = sel[1];
+        if (pass < 3 && sel[2] && prefix != 0) {  // the same in every thread
+            whole = true;
+            break;
+        }
+    }
+    const uint32_t tau = whole ? prefix - 1 : prefix, quota = whole ? 0u : krem;
+    uint32_t base_gt = 0, base_eq = 0;
+    auto write_chunk = [&](int r0) {
+        write_kept<MS, NT>(key, r0, n_total, tau, quota, base_gt, base_eq, out, budget, chunk, &tot);
+        const uint32_t c = tot;  // written before write_kept's last barrier
+        base_gt += c >> 16;
+        base_eq += c & 0xFFFFu;
+        __syncthreads();  // tot and chunk are rewritten by the next chunk
+    };
+    load_scores<MS, NT>(rows, 0, sa);
+    for (int r0 = 0; r0 < n_total; r0 += 2 * CHUNK) {
+        make_keys<MS, NT>(rows, r0, sa, key);
+        if (r0 + CHUNK < n_total) load_scores<MS, NT>(rows, r0 + CHUNK, sb);
+        write_chunk(r0);
+        if (r0 + CHUNK >= n_total) break;
+        make_keys<MS, NT>(rows, r0 + CHUNK, sb, key);
+        if (r0 + 2 * CHUNK < n_total) load_scores<MS, NT>(rows, r0 + 2 * CHUNK, sa);
+        write_chunk(r0 + CHUNK);
+    }
 }
 
 // --- multi-block selection (n_total above the on-chip bound) --------------
@@ -931,8 +1033,12 @@ KVX_API int kv_evict_topk(const float *s_kept, const float *s_new, kvx_shape sha
     const int kl = p.keep == KVX_KEEP_LOW;
     const uint32_t grid = (uint32_t)G;
     constexpr int NT = KVX_SELECT_NT;
-    static_assert(NT == 1024, "the on-chip bound assumes 1024-thread selection blocks");
-    static_assert(KVX_ONCHIP_TOTAL == 32 * NT, "keys per thread top out at 32");
+    static_assert(NT == 1024, "the on-chip bounds assume 1024-thread selection blocks");
+    static_assert(KVX_ONCHIP_TOTAL > 32 * NT, "streaming selection above the register-held keys");
+    if (need == 0 && n_total > 32 * NT) {  // keys streamed from memory at every pass
+        select_stream_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        return check_launch("kv_evict_topk");
+    }
     if (need == 0) {
         // keys per thread: the smallest power of two covering n_total (identity needs none)
         if (n_total <= NT || n_total <= p.budget)

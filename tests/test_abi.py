@@ -52,7 +52,8 @@ def test_validation_rejects_bad_calls_without_launching():
         ("kv_evict_topk", (FAKE, FAKE, sh, 0, 10, api.make_params((1 << 21) + 1, 4, 0, "low"), FAKE, None, 0, None), -2),
         ("kv_evict_topk", (FAKE, FAKE, sh, 1 << 21, (1 << 21) + 1, api.make_params(1 << 21, 4, 0, "low"), FAKE, None, 0,
                            None), -2),
-        ("kv_evict_topk", (FAKE, FAKE, sh, 0, 40000, api.make_params(20000, 4, 0, "low"), FAKE, None, 0, None), -1),
+        ("kv_evict_topk", (FAKE, FAKE, sh, 0, 300000, api.make_params(150000, 4, 0, "low"), FAKE, None, 0, None),
+         -1),                                                                       # workspace missing
         ("kv_evict_topk", (FAKE, FAKE, api.KvxShape(2, 1, 4, 32, 1), 0, 10, ok, FAKE, None, 0, None), -1),
         ("kv_evict_topk", (FAKE, FAKE, api.KvxShape(2, 1, 4, 512, 1), 0, 10, ok, FAKE, None, 0, None), -1),
         ("kv_evict_topk", (FAKE, FAKE, api.KvxShape(2, 1, 4, 128, 5), 0, 10, ok, FAKE, None, 0, None), -1),

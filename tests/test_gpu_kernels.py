@@ -141,9 +141,11 @@ SELECT_CASES = [
     (0, 8193, 8192, 4, 0, "high"), (8192, 8192, 8192, 4, 0, "high"), (8192, 8192, 8192, 4, 100, "low"),
     (0, 16384, 8192, 0, 0, "low"), (3, 5, 4, 1, 2, "high"), (0, 4097, 1, 0, 0, "low"),
     (100, 1949, 2000, 10, 30, "high"), (7, 77, 50, 49, 0, "low"),
-    # the on-chip bound (32 keys per thread) and the multi-block selection beyond it
+    # the register-held keys' bound (32 keys per thread), the streaming selection
+    # beyond it up to 262144 rows, and the multi-block selection beyond that
     (16384, 16384, 16384, 4, 0, "high"), (0, 40000, 20000, 4, 0, "low"), (20000, 20000, 20000, 4, 100, "high"),
-    (32768, 1, 32768, 4, 16, "low"), (70000, 30000, 70000, 0, 5, "low"),
+    (32768, 1, 32768, 4, 16, "low"), (70000, 30000, 70000, 0, 5, "low"), (0, 262144, 100001, 4, 0, "high"),
+    (0, 262145, 131072, 4, 8, "low"), (200000, 100000, 200000, 4, 64, "high"),
 ]
 
 
@@ -189,11 +191,13 @@ def test_multi_block_selection_checks_its_workspace():
     import torch
     api = _api()
     from kv_cache_token_amd._lib import KvxError
-    G, S, budget = 2, 40000, 20000
+    G, S, budget = 2, 300000, 150000
     shape, params = api.make_shape(1, 1, G, "bf16"), api.make_params(budget, 4, 0, "low")
     need = api.kv_evict_workspace_size(shape, 0, S, params)
-    assert need == G * (260 + 2 * 3) * 4
-    assert api.kv_evict_workspace_size(shape, 0, 30000, params) == 0       # on chip
+    assert need == G * (260 + 2 * 19) * 4                                  # 19 blocks of 16384 rows
+    assert api.kv_evict_workspace_size(shape, 0, 30000, params) == 0       # keys in registers
+    assert api.kv_evict_workspace_size(shape, 0, 262144, params) == 0      # keys streamed
+    assert api.kv_evict_workspace_size(shape, 0, 262145, params) > 0
     s = torch.zeros((G, S), device="cuda")
     idx = torch.zeros((G, budget), dtype=torch.int32, device="cuda")
     with pytest.raises(KvxError):
@@ -204,7 +208,8 @@ def test_multi_block_selection_checks_its_workspace():
 
 def test_large_budget_stream_lockstep_with_oracle():
     """Budget 20000 with 16384-token blocks: every call after the first selects
-    over more rows than fit on chip, through the multi-block path."""
+    over more rows than one workgroup holds in registers (36384: the streaming
+    selection)."""
     import torch
     from kv_cache_token_amd.cache import EvictingCache
     G, S, budget, n_sink, recent = 3, 16384, 20000, 4, 64
