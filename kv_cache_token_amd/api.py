@@ -129,9 +129,9 @@ def kv_evict_topk(s_kept, s_new, shape: KvxShape, n_kept: int, S: int, params: K
     kp = _dev(s_kept, "s_kept", torch.float32, G * params.budget, allow_none=(n_kept == 0))
     np_ = _dev(s_new, "s_new", torch.float32, G * S, allow_none=(S == 0))
     ip = _dev(keep_idx, "keep_idx", torch.int32, G * params.budget)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    return _dispatch("kv_evict_topk", (kp, np_, shape, n_kept, S, params, ip,
-                                       None if ws is None else ws.data_ptr(), wsb, _stream(stream)), prepare)
+    wp = _dev(ws, "ws", torch.uint8, 0, allow_none=True)  # its size is checked by the library
+    wsb = 0 if ws is None else ws.numel()
+    return _dispatch("kv_evict_topk", (kp, np_, shape, n_kept, S, params, ip, wp, wsb, _stream(stream)), prepare)
 
 
 def kv_compact_gather(k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, pos_base: int, keep_idx,
@@ -246,6 +246,8 @@ def qf_filters_from_keys(k: np.ndarray, n: int, dtype: str = "bf16") -> np.ndarr
     G, rows, Dd = k.shape
     if k.dtype not in (np.float32, np.uint16):
         raise TypeError("keys must be float32 or 16-bit bits (uint16)")
+    if k.dtype == np.uint16 and dtype not in ("bf16", "f16"):
+        raise ValueError("16-bit key bits need dtype 'bf16' or 'f16', got %r" % (dtype,))
     dt = KVX_F32 if k.dtype == np.float32 else (KVX_F16 if dtype == "f16" else KVX_BF16)
     out = np.empty((G, Dd), dtype=np.float32)
     call("qf_filters_from_keys", k.ctypes.data, dt, G, n, rows, Dd, out.ctypes.data)

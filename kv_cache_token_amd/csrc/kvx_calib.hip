@@ -20,12 +20,13 @@
 // accumulator tiles of 16 x 16: a pass over the rows for the fp64 column sums,
 // a pass that stages chunks of rows (centred when asked) in LDS as fp64 and
 // feeds them four rows at a time to the tiles, then power iteration with C
-// held in the tiles, and a bounded second iteration on the complement of the
-// found vector that checks that the top eigenvalue is separated.  When the
-// iteration is slow (top two eigenvalues close), C is squared in place every 32
-// steps (C staged in LDS, the product again on the matrix cores; up to 2^10-th
-// powers, rescaled by a power of two): the eigenvectors stay, the ratio of the
-// top two eigenvalues is squared.
+// held in the tiles, and a check that the top eigenvalue is separated: first a
+// bound from the Frobenius norm (on C, then on C^2), else a bounded second
+// iteration on the complement of the found vector.  While the iteration is
+// slow (top two eigenvalues close), C is squared in place every
+// KVX_SQUARE_EVERY steps (C staged in LDS, the product again on the matrix
+// cores; up to 2^10-th powers, rescaled by a power of two): the eigenvectors
+// stay, the ratio of the top two eigenvalues is squared.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
