@@ -457,7 +457,9 @@ def bench_qcal(torch, args):
         event_times(torch, st, fn, args.warmup)
     ms = event_times(torch, st, fn, args.steps)
     assert int(status.max()) == 0
-    flops = 2.0 * N * D * D * Hq * L            # the Gram matrices (power iteration not counted)
+    # the Gram matrices: D (D + 1) / 2 distinct entries of a symmetric D x D
+    # matrix, 2 N flops each (power iteration and squarings not counted)
+    flops = float(N * D * (D + 1) * Hq * L)
     achieved = flops / (ms * 1e-3) / 1e12
     out_line = {
         "metric": "query-SVD calibration query heads/sec (fp64 Gram + power iteration + GQA averaging)",
@@ -468,7 +470,7 @@ def bench_qcal(torch, args):
         "config": {"workload": DESCRIPTIONS["qcal"], "device": torch.cuda.get_device_name(0)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP64_TFLOPS, 4), "traffic": None,
-                     "kernel": "top_direction_kernel (Gram flops only)",
+                     "kernel": "top_direction_kernel (symmetric Gram flops only)",
                      "algorithmic_flops_per_launch": int(flops), "mean_launch_us": round(ms * 1e3, 1)},
     }
     if not args.no_cpu_baseline:

@@ -89,10 +89,38 @@ struct DirLayout {
     static constexpr int QW = HD / 64;     // quadrants of C per side
     static constexpr int NT = 64 * QW * QW;  // one wave per quadrant: 64 threads for HD 64, 256 for HD 128
     static constexpr int CH = HD;          // staged rows per chunk: an HD x HD fp64 square of LDS
-    static constexpr int S = HD + 1;       // LDS row stride in doubles (column reads hit distinct banks)
+    static constexpr int S = HD + 1;       // LDS row stride in doubles of C (column reads hit distinct banks)
+    // Staged rows: column c at c + c / 8 (a gap after every 8 columns, so that
+    // the 16 lanes of a row, each writing its 8 consecutive columns, hit
+    // distinct banks), rows SP doubles apart
+    static constexpr int SP = HD + HD / 8 + 1;
     static constexpr int SQUARE_EVERY = KVX_SQUARE_EVERY;  // power steps between squarings of C
     static constexpr int MAX_SQUARINGS = 10;
     static_assert(QW == 1 || QW == 2, "the device estimator covers head dims 64 and 128");
+};
+
+// C is symmetric, so the Gram pass accumulates only its 16 x 16 tiles (i, j)
+// with i <= j (36 of 64 at head dim 128), spread evenly over the waves.  A
+// pattern names the wave's operand slots (each holds the rows' entries of one
+// 16-column block) and, per tile, the two slots it multiplies.  Head dim 64
+// (one wave): the upper triangle of the 4 x 4 tiles.  Head dim 128: a wave of
+// a diagonal quadrant takes that quadrant's upper triangle except its tile
+// (1, 1); the two other waves split the off-diagonal quadrant by tile rows and
+// each takes one of the two tiles left over.
+struct GramUpper {  // slots: the quadrant's four column blocks
+    static constexpr int kSlots = 4, kTiles = 10;
+    static constexpr int ta[kTiles] = {0, 0, 0, 0, 1, 1, 1, 2, 2, 3};
+    static constexpr int tb[kTiles] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
+};
+struct GramDiag {  // as GramUpper without tile (1, 1)
+    static constexpr int kSlots = 4, kTiles = 9;
+    static constexpr int ta[kTiles] = {0, 0, 0, 0, 1, 1, 2, 2, 3};
+    static constexpr int tb[kTiles] = {0, 1, 2, 3, 2, 3, 2, 3, 3};
+};
+struct GramOff {  // slots: two row blocks, column blocks 4-7, a diagonal quadrant's block 1
+    static constexpr int kSlots = 7, kTiles = 9;
+    static constexpr int ta[kTiles] = {0, 0, 0, 0, 1, 1, 1, 1, 6};
+    static constexpr int tb[kTiles] = {2, 3, 4, 5, 2, 3, 4, 5, 6};
 };
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -121,10 +149,11 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
     int32_t *__restrict__ status, int max_iter) {
     using L = DirLayout<HD>;
     using R = Row<DT, HD>;
-    constexpr int NT = L::NT, CH = L::CH, S = L::S, E = R::kElemsPerLane, SLOTS = NT / R::kLanes;
+    constexpr int NT = L::NT, CH = L::CH, S = L::S, SP = L::SP, E = R::kElemsPerLane, SLOTS = NT / R::kLanes;
+    static_assert(CH * SP >= HD * S, "C fits the staging buffer");
     static_assert(SLOTS >= 1 && NT % R::kLanes == 0, "a workgroup covers whole rows");
     static_assert(SLOTS <= CH, "the column partial sums fit the staging buffer");
-    __shared__ double xd[CH * S];  // staged rows, or C while it is squared; first the column partial sums
+    __shared__ double xd[CH * SP];  // staged rows, or C; first the column partial sums
     __shared__ double cs[HD], mu[HD], v[HD], y[HD], w[HD], acc[HD], yp[L::QW][HD], lam[2], red[NT / 64],
         fr[NT / 64];
     __shared__ int flag;
@@ -254,6 +283,64 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
         }
     };
 
+    // This wave's Gram pattern and the 16-column block of each operand slot
+    // (off the diagonal, wave 1 takes rows 0-31 and tile (1, 1), wave 2 rows
+    // 32-63 and tile (5, 5)).
+    const bool diag = R0 == C0;
+    int blk[GramOff::kSlots];
+#pragma unroll
+    for (int sl = 0; sl < GramOff::kSlots; ++sl)
+        blk[sl] = diag ? R0 / 16 + min(sl, 3)
+                       : (sl < 2 ? 2 * (wv - 1) + sl : (sl < 6 ? 2 + sl : (wv == 1 ? 1 : 5)));
+    // Gram steps 0 .. steps-1 of the staged chunk (rows 4s .. 4s+3): slot
+    // operands X[k][16 blk + lr] (at column 18 blk + lr + lr / 8 of the staged
+    // layout) of the next step are read from LDS before this step's products
+    // are issued (two operand sets used in turn), so the matrix cores do not
+    // wait for them
+    auto gram_steps = [&](auto pattern, int steps) {
+        using P = decltype(pattern);
+        double o0[P::kSlots], o1[P::kSlots];
+        auto operands = [&](int st, double *o) {
+            const int k = 4 * st + lk;
+#pragma unroll
+            for (int sl = 0; sl < P::kSlots; ++sl) o[sl] = xd[k * SP + 18 * blk[sl] + lr + (lr >> 3)];
+        };
+        auto products = [&](const double *o) {
+#pragma unroll
+            for (int u = 0; u < P::kTiles; ++u)
+                Cm[u / 4][u % 4] = mfma16x16x4(o[P::ta[u]], o[P::tb[u]], Cm[u / 4][u % 4]);
+        };
+        // the next set is read even past the last step (a repeat of the last
+        // one, unused), so the loads do not depend on the step count; the
+        // scheduling barriers keep each set's loads ahead of the other set's
+        // products, so every product waits only for operands read a step
+        // earlier
+        operands(0, o0);
+        for (int st = 0; st < steps; st += 2) {
+            operands(min(st + 1, steps - 1), o1);
+            __builtin_amdgcn_sched_barrier(0);
+            products(o0);
+            __builtin_amdgcn_sched_barrier(0);
+            operands(min(st + 2, steps - 1), o0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (st + 1 < steps) products(o1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto gram_to_lds = [&](auto pattern) {
+        using P = decltype(pattern);
+#pragma unroll
+        for (int u = 0; u < P::kTiles; ++u) {
+            const int bi = blk[P::ta[u]], bj = blk[P::tb[u]];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = 16 * bi + lk + 4 * q, j = 16 * bj + lr;
+                xd[i * S + j] = Cm[u / 4][u % 4][q];
+                if (bi != bj) xd[j * S + i] = Cm[u / 4][u % 4][q];
+            }
+        }
+    };
+
     for (int i = t; i < HD; i += NT) acc[i] = 0.0;
     int worst = 0;
     for (int q = 0; q < r; ++q) {
@@ -303,8 +390,10 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
             reduce_sums();
         }
         // Gram matrix of the (centred) rows: A = X^T and B = X, four rows a
-        // step.  The loads of chunk c + 1 are in flight while chunk c is on the
-        // matrix cores; rows past a chunk read its last row and are not used.
+        // step, upper tiles only (GramUpper / GramDiag / GramOff) accumulated in
+        // the first entries of Cm.  The loads of chunk c + 1 are in flight while chunk c
+        // is on the matrix cores; rows past a chunk read its last row and are
+        // not used.
         zero_c();
         uint4 raw[kPer];
         auto fetch = [&](int64_t base) {
@@ -324,7 +413,10 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
                 const int rr = (t + u * NT) / R::kLanes;
                 if (rr >= rows) {  // past the chunk's end: zeros, so that steps need no bound checks
 #pragma unroll
-                    for (int k = 0; k < E; ++k) xd[rr * S + part * E + k] = 0.0;
+                    for (int k = 0; k < E; ++k) {
+                        const int c = part * E + k;
+                        xd[rr * SP + c + (c >> 3)] = 0.0;
+                    }
                     continue;
                 }
                 float f[E];
@@ -333,9 +425,9 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
                 for (int k = 0; k < E; ++k) {
                     const int c = part * E + k;
                     if constexpr (MODE == DIR_CENTRED_KEYS) {
-                        xd[rr * S + c] = (double)f[k] - mu[c];
+                        xd[rr * SP + c + (c >> 3)] = (double)f[k] - mu[c];
                     } else {
-                        xd[rr * S + c] = (double)f[k];
+                        xd[rr * SP + c + (c >> 3)] = (double)f[k];
                         csum[k] += (double)f[k];
                     }
                 }
@@ -346,30 +438,30 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
             // operands of the next step are read from LDS before this step's
             // products are issued, so the matrix cores do not wait for them
             const int steps = (rows + 3) >> 2;
-            double a0[4], b0[4], a1[4], b1[4];  // two operand sets, used in turn
-            auto operands = [&](int s, double *a_, double *b_) {
-                const int k = 4 * s + lk;
-#pragma unroll
-                for (int a = 0; a < 4; ++a) a_[a] = xd[k * S + R0 + 16 * a + lr];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) b_[b] = xd[k * S + C0 + 16 * b + lr];
-            };
-            auto products = [&](const double *a_, const double *b_) {
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) Cm[a][b] = mfma16x16x4(a_[a], b_[b], Cm[a][b]);
-            };
-            operands(0, a0, b0);
-            int s = 0;
-            for (; s + 1 < steps; s += 2) {
-                operands(s + 1, a1, b1);
-                products(a0, b0);
-                if (s + 2 < steps) operands(s + 2, a0, b0);
-                products(a1, b1);
-            }
-            if (s < steps) products(a0, b0);
+            if constexpr (L::QW == 1)
+                gram_steps(GramUpper{}, steps);
+            else if (diag)
+                gram_steps(GramDiag{}, steps);
+            else
+                gram_steps(GramOff{}, steps);
         }
+        // C from the upper tiles: each tile to its place in xd and, off the
+        // diagonal, its transpose to the mirrored place; then every wave loads
+        // its whole quadrant into Cm
+        __syncthreads();  // the last chunk's products have read xd
+        if constexpr (L::QW == 1)
+            gram_to_lds(GramUpper{});
+        else if (diag)
+            gram_to_lds(GramDiag{});
+        else
+            gram_to_lds(GramOff{});
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) Cm[a][b][q] = xd[(R0 + 16 * a + lk + 4 * q) * S + C0 + 16 * b + lr];
         if constexpr (MODE == DIR_RAW_QUERIES) reduce_sums();  // begins with a barrier
         __syncthreads();
 
