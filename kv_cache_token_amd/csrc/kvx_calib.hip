@@ -390,10 +390,10 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
             reduce_sums();
         }
         // Gram matrix of the (centred) rows: A = X^T and B = X, four rows a
-        // step, upper tiles only (GramUpper / GramDiag / GramOff) accumulated in
-        // the first entries of Cm.  The loads of chunk c + 1 are in flight while chunk c
-        // is on the matrix cores; rows past a chunk read its last row and are
-        // not used.
+        // step, upper tiles only (GramUpper / GramDiag / GramOff) accumulated
+        // in the first entries of Cm.  The loads of chunk c + 1 are in flight
+        // while chunk c is on the matrix cores; rows past a chunk read its last
+        // row and are not used.
         zero_c();
         uint4 raw[kPer];
         auto fetch = [&](int64_t base) {
