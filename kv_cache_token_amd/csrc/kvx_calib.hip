@@ -131,6 +131,34 @@ __device__ __forceinline__ f64x4 mfma16x16x4(double a, double b, f64x4 c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
+// x of another lane by a DPP move of its two 32-bit halves (CTRL: a quad
+// permute or a row rotation; every lane reads a valid source).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+// op over the 64 lanes of a wave, the result in every lane: pairs and quads
+// by quad permutes, the four quads of a row by rotating the row by 4 and 8
+// lanes, the four rows by reading one lane of each (all on the vector unit's
+// lane network, no LDS round trips).
+template <class Op>
+__device__ __forceinline__ double wave_reduce_f64(double s, Op op) {
+    s = op(s, dpp_f64<0xB1>(s));   // quad_perm [1, 0, 3, 2]
+    s = op(s, dpp_f64<0x4E>(s));   // quad_perm [2, 3, 0, 1]
+    s = op(s, dpp_f64<0x124>(s));  // row_ror:4
+    s = op(s, dpp_f64<0x128>(s));  // row_ror:8
+    return op(op(readlane_f64(s, 0), readlane_f64(s, 16)), op(readlane_f64(s, 32), readlane_f64(s, 48)));
+}
+
 __device__ __forceinline__ double shfl_xor_f64(double x, int off) {
     const unsigned long long u = (unsigned long long)__double_as_longlong(x);
     const uint32_t lo = __shfl_xor((uint32_t)u, off), hi = __shfl_xor((uint32_t)(u >> 32), off);
@@ -154,7 +182,11 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
     static_assert(SLOTS >= 1 && NT % R::kLanes == 0, "a workgroup covers whole rows");
     static_assert(SLOTS <= CH, "the column partial sums fit the staging buffer");
     __shared__ double xd[CH * SP];  // staged rows, or C; first the column partial sums
-    __shared__ double cs[HD], mu[HD], v[HD], y[HD], w[HD], acc[HD], yp[L::QW][HD], lam[2], red[NT / 64],
+    // ypb: quadrant column sums of a mat-vec, two buffers used in turn by the
+    // power iteration (the other mat-vecs use the first); vw: each wave's copy
+    // of the power iteration's iterate
+    __shared__ double cs[HD], mu[HD], v[HD], y[HD], w[HD], acc[HD], ypb[2][L::QW][HD], vw[NT / 64][HD],
+        lam[2], red[NT / 64],
         fr[NT / 64];
     __shared__ int flag;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -172,9 +204,9 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
     };
     // y = C x, as C^T x (C is symmetric): each lane sums its 16 entries of a
     // column, the four lanes of a column meet by two shuffles, and each
-    // quadrant's column sums go to yp (ends with a barrier); wave 0 then adds
+    // quadrant's column sums go to ypb[0] (ends with a barrier); wave 0 then adds
     // the quadrants of a column band (gather_y)
-    auto matvec = [&](const double *xv) {
+    auto matvec = [&](const double *xv) __attribute__((always_inline)) {
         double p[4] = {0.0, 0.0, 0.0, 0.0};  // p[b]: part of y[C0 + 16b + lr]
 #pragma unroll
         for (int a = 0; a < 4; ++a)
@@ -191,23 +223,20 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
         }
         if (lk == 0)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) yp[wv / L::QW][C0 + 16 * b + lr] = p[b];
+            for (int b = 0; b < 4; ++b) ypb[0][wv / L::QW][C0 + 16 * b + lr] = p[b];
         __syncthreads();
     };
     auto gather_y = [&]() {  // wave 0
         for (int i = lane; i < HD; i += 64) {
-            double s = yp[0][i];
+            double s = ypb[0][0][i];
 #pragma unroll
-            for (int h = 1; h < L::QW; ++h) s += yp[h][i];
+            for (int h = 1; h < L::QW; ++h) s += ypb[0][h][i];
             y[i] = s;
         }
     };
     // wave-0 reductions and vector updates over HD-long LDS vectors
-    auto wsum = [&](double s) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) s += shfl_xor_f64(s, off);
-        return s;
-    };
+    auto wsum = [&](double s) { return wave_reduce_f64(s, [](double a, double b) { return a + b; }); };
+    auto wmax = [&](double s) { return wave_reduce_f64(s, [](double a, double b) { return fmax(a, b); }); };
     auto wdot = [&](const double *a, const double *b) {
         double s = 0.0;
         for (int i = lane; i < HD; i += 64) s += a[i] * b[i];
@@ -228,59 +257,68 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
             dmax = fmax(dmax, fabs(nv - xv[i]));
             xv[i] = nv;
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) dmax = fmax(dmax, shfl_xor_f64(dmax, off));
+        dmax = wmax(dmax);
         return !(ss > 0.0) ? 2 : (dmax < 1e-14 ? 1 : 0);
     };
-    // C <- C C / 2^e (C symmetric: row k of C is column k), e the exponent of
-    // the largest entry of C C; ends with a barrier
-    auto square = [&]() {
-        __syncthreads();  // nobody reads xd any more
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) xd[(R0 + 16 * a + lk + 4 * q) * S + C0 + 16 * b + lr] = Cm[a][b][q];
-        __syncthreads();
-        zero_c();
-        for (int k0 = 0; k0 < HD; k0 += 4) {
-            double av[4], bv[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) av[a] = xd[(R0 + 16 * a + lr) * S + k0 + lk];  // A[i][k] = C[i][k]
-#pragma unroll
-            for (int b = 0; b < 4; ++b) bv[b] = xd[(k0 + lk) * S + C0 + 16 * b + lr];  // B[k][j] = C[k][j]
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) Cm[a][b] = mfma16x16x4(av[a], bv[b], Cm[a][b]);
-        }
-        double m = 0.0;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) m = fmax(m, fabs(Cm[a][b][q]));
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmax(m, shfl_xor_f64(m, off));
-        if (lane == 0) red[t / 64] = m;
-        __syncthreads();
-        double mx = 0.0;
-        for (int i = 0; i < NT / 64; ++i) mx = fmax(mx, red[i]);
-        const double scale = mx > 0.0 ? ldexp(1.0, -ilogb(mx)) : 1.0;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) Cm[a][b] *= scale;
-        __syncthreads();  // red and xd are free again
-    };
     // a fixed, generic start vector
+    auto start_value = [](int i, uint32_t salt) {
+        const uint32_t h = ((uint32_t)(i + 1) ^ salt) * 2654435761u;
+        return ((h >> 31) ? -1.0 : 1.0) * (0.5 + (double)((h >> 8) & 0xFFFF) / 65536.0);
+    };
     auto start = [&](double *xv, uint32_t salt) {
-        for (int i = t; i < HD; i += NT) {
-            const uint32_t h = ((uint32_t)(i + 1) ^ salt) * 2654435761u;
-            xv[i] = ((h >> 31) ? -1.0 : 1.0) * (0.5 + (double)((h >> 8) & 0xFFFF) / 65536.0);
+        for (int i = t; i < HD; i += NT) xv[i] = start_value(i, salt);
+    };
+    // One power step on this wave's copy of the iterate: the mat-vec's
+    // quadrant sums go to ypb[k] and meet after one barrier; then every wave
+    // adds them and normalises by itself (the same operations on the same
+    // values, so every copy stays equal and every wave returns the same
+    // verdict: 2 for a zero result, 1 when no entry moved by 1e-14, else 0).
+    // With the two buffers used in turn one barrier per step suffices: a wave
+    // rewrites ypb[k] only after the next step's barrier, which every wave
+    // passes after its reads of ypb[k].
+    auto power_step = [&](int k) __attribute__((always_inline)) {
+        double *xv = vw[wv];
+        double p[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double xi = xv[R0 + 16 * a + lk + 4 * q];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) p[b] = __builtin_fma(Cm[a][b][q], xi, p[b]);
+            }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            p[b] += shfl_xor_f64(p[b], 16);
+            p[b] += shfl_xor_f64(p[b], 32);
         }
+        if (lk == 0)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) ypb[k][wv / L::QW][C0 + 16 * b + lr] = p[b];
+        __syncthreads();
+        constexpr int J = HD / 64;
+        double yv[J], ss = 0.0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int i = lane + 64 * j;
+            double s = ypb[k][0][i];
+#pragma unroll
+            for (int h = 1; h < L::QW; ++h) s += ypb[k][h][i];
+            yv[j] = s;
+            ss += s * s;
+        }
+        ss = wsum(ss);
+        const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+        double dmax = 0.0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int i = lane + 64 * j;
+            const double nv = yv[j] * inv;
+            dmax = fmax(dmax, fabs(nv - xv[i]));
+            xv[i] = nv;
+        }
+        dmax = wmax(dmax);
+        return !(ss > 0.0) ? 2 : (dmax < 1e-14 ? 1 : 0);
     };
 
     // This wave's Gram pattern and the 16-column block of each operand slot
@@ -297,7 +335,7 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
     // layout) of the next step are read from LDS before this step's products
     // are issued (two operand sets used in turn), so the matrix cores do not
     // wait for them
-    auto gram_steps = [&](auto pattern, int steps) {
+    auto gram_steps = [&](auto pattern, int steps) __attribute__((always_inline)) {
         using P = decltype(pattern);
         double o0[P::kSlots], o1[P::kSlots];
         auto operands = [&](int st, double *o) {
@@ -327,7 +365,7 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto gram_to_lds = [&](auto pattern) {
+    auto gram_to_lds = [&](auto pattern) __attribute__((always_inline)) {
         using P = decltype(pattern);
 #pragma unroll
         for (int u = 0; u < P::kTiles; ++u) {
@@ -339,6 +377,73 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
                 if (bi != bj) xd[j * S + i] = Cm[u / 4][u % 4][q];
             }
         }
+    };
+
+    // every wave's quadrant of C from xd (row stride S); ends with a barrier
+    auto quadrant_from_lds = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) Cm[a][b][q] = xd[(R0 + 16 * a + lk + 4 * q) * S + C0 + 16 * b + lr];
+        __syncthreads();
+    };
+    // the upper tiles in Cm to their places in xd and the mirrored ones, then
+    // every wave's quadrant back into Cm; begins and ends with a barrier
+    auto symmetric_c = [&]() __attribute__((always_inline)) {
+        __syncthreads();  // the products have read xd
+        if constexpr (L::QW == 1)
+            gram_to_lds(GramUpper{});
+        else if (diag)
+            gram_to_lds(GramDiag{});
+        else
+            gram_to_lds(GramOff{});
+        __syncthreads();
+        quadrant_from_lds();
+    };
+    // C <- C C / 2^e, e the exponent of the largest entry of C C.  C is
+    // symmetric, so C C = C^T C is the Gram matrix of C's rows: C goes to xd
+    // in the staged-row layout and the Gram pass's products make the upper
+    // tiles.  Ends with a barrier.
+    auto square = [&]() __attribute__((always_inline)) {
+        __syncthreads();  // nobody reads xd any more
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = C0 + 16 * b + lr;
+                    xd[(R0 + 16 * a + lk + 4 * q) * SP + c + (c >> 3)] = Cm[a][b][q];
+                }
+        __syncthreads();
+        zero_c();
+        if constexpr (L::QW == 1)
+            gram_steps(GramUpper{}, HD / 4);
+        else if (diag)
+            gram_steps(GramDiag{}, HD / 4);
+        else
+            gram_steps(GramOff{}, HD / 4);
+        symmetric_c();
+        double m = 0.0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) m = fmax(m, fabs(Cm[a][b][q]));
+        m = wmax(m);
+        if (lane == 0) red[t / 64] = m;
+        __syncthreads();
+        double mx = 0.0;
+        for (int i = 0; i < NT / 64; ++i) mx = fmax(mx, red[i]);
+        const double scale = mx > 0.0 ? ldexp(1.0, -ilogb(mx)) : 1.0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) Cm[a][b] *= scale;
+        __syncthreads();  // red and xd are free again
     };
 
     for (int i = t; i < HD; i += NT) acc[i] = 0.0;
@@ -448,39 +553,17 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
         // C from the upper tiles: each tile to its place in xd and, off the
         // diagonal, its transpose to the mirrored place; then every wave loads
         // its whole quadrant into Cm
-        __syncthreads();  // the last chunk's products have read xd
-        if constexpr (L::QW == 1)
-            gram_to_lds(GramUpper{});
-        else if (diag)
-            gram_to_lds(GramDiag{});
-        else
-            gram_to_lds(GramOff{});
-        __syncthreads();
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) Cm[a][b][q] = xd[(R0 + 16 * a + lk + 4 * q) * S + C0 + 16 * b + lr];
+        symmetric_c();
         if constexpr (MODE == DIR_RAW_QUERIES) reduce_sums();  // begins with a barrier
         __syncthreads();
 
-        // power iteration; `flag` carries wave 0's verdict to the workgroup
-        start(v, 0u);
-        __syncthreads();
+        // power iteration (power_step: every wave on its own copy of the
+        // iterate, every wave taking the same decisions)
+        for (int i = lane; i < HD; i += 64) vw[wv][i] = start_value(i, 0u);
         int calm = 0, it = 0, f = 0, squarings = 0;
         double power = 1.0;  // C now holds the original C to this power
-        // (flag and lam are rewritten by wave 0 only after the next mat-vec's
-        // barrier, which every thread reaches after reading them)
         for (; it < max_iter; ++it) {
-            matvec(v);
-            if (t < 64) {
-                gather_y();
-                const int rc = renorm(v, y, nullptr);
-                if (lane == 0) flag = rc;
-            }
-            __syncthreads();
-            f = flag;
+            f = power_step(it & 1);
             if (f == 2) break;
             calm = f == 1 ? calm + 1 : 0;
             if (calm >= 2) break;
@@ -491,6 +574,9 @@ __global__ __launch_bounds__(DirLayout<HD>::NT) void top_direction_kernel(
                 calm = 0;
             }
         }
+        if (wv == 0)
+            for (int i = lane; i < HD; i += 64) v[i] = vw[0][i];
+        __syncthreads();
         int st = f == 2 ? 2 : (calm >= 2 ? 0 : 1);
         double fro_all = 0.0;  // |C|_F^2 of the current C, summed over the workgroup
         if (st == 0) {
