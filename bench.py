@@ -594,6 +594,13 @@ def main():
     per = kernel_times(torch, wl, args.steps)
     breakdown = {n: {"launches_per_step": len(v) // args.steps, "mean_us": round(1e3 * sum(v) / len(v), 2)}
                  for n, v in per.items()}
+    chunk_sizes = {k.shape[1] for k, _ in wl.blocks}
+    if "qf_score_keys" in breakdown and len(chunk_sizes) == 1:
+        # scoring reads each incoming row once and writes its score
+        sb = cfg.G // args.split * chunk_sizes.pop() * (wl.row + 4)
+        e = breakdown["qf_score_keys"]
+        e["algorithmic_bytes_per_launch"] = sb
+        e["GBps"] = round(sb / (e["mean_us"] * 1e-6) / 1e9, 1)
     dom_ms = per[wl.dominant]
     if wl.dominant == "kv_compact_gather":
         # evicting launches only: the leading calls of each run that only append are left out
