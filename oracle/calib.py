@@ -15,7 +15,9 @@ return float64; callers round to float32 where the pages store float32 filters.
   "Key-SVD fallback": top right singular vector of the mean-centred first
   calib_tokens keys.  The pages call its sign ambiguous; after centring
   1^T u1 is identically zero, so the reading used here fixes the sign by making
-  the entry of largest magnitude positive (lowest index on exact ties).
+  the entry of largest magnitude positive (lowest index on exact ties).  That
+  sign rule is parity unpinned: the pages fix no sign for this source, so it is
+  checked for self-consistency only (the direction itself is pinned).
 
 Degenerate inputs (sigma_1 == sigma_2 up to 1e-12 relative, zero matrices,
 a zero group mean, sgn(0)) follow the readings listed in the design notes:
