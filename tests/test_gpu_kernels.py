@@ -96,6 +96,28 @@ def test_score_within_tolerance(dtype, mode, sign, Dd):
         assert np.array_equal(got[nz], -pos[nz])          # sign is an exact negation
 
 
+@pytest.mark.parametrize("mode,sign", [("l2", 1), ("proj", -1)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_score_tolerance_holds_across_the_float32_range(dtype, mode, sign):
+    """Keys scaled by 2^50 and 2^-55 (every square or product still a normal
+    float32) score within the same tolerance as keys of order one."""
+    L, B, H, S = 1, 1, 4, 300
+    G = L * B * H
+    say("score range %s %s %d" % (dtype, mode, sign))
+    rng = np.random.default_rng(7)
+    f_lh = rng.standard_normal((L, H, D)).astype(np.float32) if mode == "proj" else None
+    if f_lh is not None:
+        f_lh /= np.linalg.norm(f_lh, axis=2, keepdims=True)
+    fg = _group_filters(f_lh, L, B, H) if mode == "proj" else [None] * G
+    for e in (50, -55):
+        K = np.stack([synth.custom_keys((S, D), 700 + g, dtype, scale=2.0 ** e) for g in range(G)])
+        got = _score_gpu(K, dtype, mode, f_lh, sign, L, B, H)
+        want = np.stack([oracle.score(K[g], mode, fg[g], sign, dtype) for g in range(G)])
+        scale = np.stack([score_scale(K[g], dtype, mode, fg[g]) for g in range(G)])
+        assert np.all(np.isfinite(got)) and np.all(np.abs(want) > 0)
+        assert_scores_close(got, want, scale, "scale 2^%d" % e)
+
+
 def test_score_independent_of_block_split_and_negative_zero():
     import torch
     api = _api()
