@@ -80,6 +80,7 @@ extern "C" {
 #define KVX_MAX_BUDGET (1 << 21)   /* largest budget accepted                          */
 #define KVX_MAX_TOTAL (1 << 22)    /* largest n_kept + S that one selection handles     */
 #define KVX_ONCHIP_TOTAL 262144    /* up to this n_total the selection needs no workspace */
+#define KVX_NOALLOC_SCRATCH_BYTES (8 << 20) /* static device scratch of kv_evict_topk_noalloc */
 
 typedef struct {
     int64_t L, B, H; /* layers, batch, KV heads: G = L*B*H groups            */
@@ -172,6 +173,23 @@ KVX_API int kv_evict_workspace_size(kvx_shape shape, int64_t n_kept, int64_t S,
 KVX_API int kv_evict_topk(const float *s_kept, const float *s_new, kvx_shape shape,
                           int64_t n_kept, int64_t S, kvx_evict_params p, int32_t *keep_idx,
                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * kv_evict_topk_noalloc -- kv_evict_topk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, rules, output and errors as
+ * kv_evict_topk, without the workspace: where kv_evict_workspace_size would
+ * be non-zero, the selection uses a static device array of
+ * KVX_NOALLOC_SCRATCH_BYTES (8 MiB) that the library holds on every GPU it
+ * runs on until the process ends, and sizes whose workspace would exceed it
+ * return KVX_ERANGE before anything is enqueued.  Nothing is allocated or
+ * freed by this call.  The array is cleared by a fill kernel on `stream` at
+ * the start of each call that uses it; every call on one GPU shares it, so
+ * calls that overlap on one GPU (other streams, other host threads) race.
+ * `stream` must belong to the current device (KVX_EINVAL otherwise).
+ */
+KVX_API int kv_evict_topk_noalloc(const float *s_kept, const float *s_new, kvx_shape shape, int64_t n_kept,
+                                  int64_t S, kvx_evict_params p, int32_t *keep_idx, void *stream);
 
 /*
  * kv_compact_gather -- step 4: copy the survivors in temporal order.

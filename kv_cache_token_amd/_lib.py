@@ -17,6 +17,7 @@ KVX_F32, KVX_BF16, KVX_F16 = 0, 1, 2
 KVX_SCORE_L2, KVX_SCORE_PROJ, KVX_SCORE_CACHE_KEYS = 0, 1, 0x100
 KVX_KEEP_HIGH, KVX_KEEP_LOW = 0, 1
 KVX_HEAD_DIM, KVX_MAX_BUDGET, KVX_MAX_TOTAL, KVX_ONCHIP_TOTAL = 128, 1 << 21, 1 << 22, 1 << 18
+KVX_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 _CODES = {KVX_EINVAL: "EINVAL", KVX_ERANGE: "ERANGE", KVX_EDEVICE: "EDEVICE", KVX_EIO: "EIO",
           KVX_EMISMATCH: "EMISMATCH"}
@@ -55,6 +56,7 @@ _SIGS = {
     "qf_score_keys": ([_vp, KvxShape, _i64, _i32, _vp, _i32, _vp, _vp], ctypes.c_int),
     "kv_evict_workspace_size": ([KvxShape, _i64, _i64, KvxParams, ctypes.POINTER(_sz)], ctypes.c_int),
     "kv_evict_topk": ([_vp, _vp, KvxShape, _i64, _i64, KvxParams, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "kv_evict_topk_noalloc": ([_vp, _vp, KvxShape, _i64, _i64, KvxParams, _vp, _vp], ctypes.c_int),
     "kv_compact_gather": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, KvxShape, _i64, _i64, KvxParams,
                            _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "kv_evict_one_inplace": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, KvxShape, _i64, KvxParams, _vp],

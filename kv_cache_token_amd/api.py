@@ -134,6 +134,18 @@ def kv_evict_topk(s_kept, s_new, shape: KvxShape, n_kept: int, S: int, params: K
     return _dispatch("kv_evict_topk", (kp, np_, shape, n_kept, S, params, ip, wp, wsb, _stream(stream)), prepare)
 
 
+def kv_evict_topk_noalloc(s_kept, s_new, shape: KvxShape, n_kept: int, S: int, params: KvxParams, keep_idx,
+                          stream=None, prepare: bool = False):
+    """kv_evict_topk without a workspace argument: the library's static device
+    scratch serves the selections that need one (allocation-free callers)."""
+    torch = _torch()
+    G = _G(shape)
+    kp = _dev(s_kept, "s_kept", torch.float32, G * params.budget, allow_none=(n_kept == 0))
+    np_ = _dev(s_new, "s_new", torch.float32, G * S, allow_none=(S == 0))
+    ip = _dev(keep_idx, "keep_idx", torch.int32, G * params.budget)
+    return _dispatch("kv_evict_topk_noalloc", (kp, np_, shape, n_kept, S, params, ip, _stream(stream)), prepare)
+
+
 def kv_compact_gather(k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new, pos_base: int, keep_idx,
                       shape: KvxShape, n_kept: int, S: int, params: KvxParams, k_out, v_out, s_out, pos_out,
                       stream=None, prepare: bool = False):

@@ -11,11 +11,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "kvevict.h"
 #include "kvx_common.h"
 #include "kvx_rows.h"
+
+// The allocation-free selection's workspace (kv_evict_topk_noalloc): a fixed
+// array in device memory that every GPU the library runs on holds until the
+// process ends.  In host code its name stands for a host-side handle, not a
+// device address, so host code only ever uses the address that
+// scratch_address() looks up per device.
+static __device__ __align__(256) uint32_t scratch[KVX_NOALLOC_SCRATCH_BYTES / 4];
 
 namespace kvx {
 namespace {
@@ -961,6 +969,89 @@ int launch_gather(const void *k_kept, const void *v_kept, const float *s_kept, c
     return check_launch("kv_compact_gather");
 }
 
+// Selection launches after validation.  `ws` is the multi-block selection's
+// workspace (nullptr when it selects on chip).
+int launch_select(const float *s_kept, const float *s_new, int64_t G, int64_t n_kept, int64_t S,
+                  const kvx_evict_params &p, int32_t *keep_idx, uint32_t *ws, hipStream_t st, const char *what) {
+    const int64_t n_total = n_kept + S;
+    const int a = (int)n_kept, b = (int)S, bud = (int)p.budget, ns = (int)p.n_sink, rc2 = (int)p.recent;
+    const int kl = p.keep == KVX_KEEP_LOW;
+    const uint32_t grid = (uint32_t)G;
+    constexpr int NT = KVX_SELECT_NT;
+    static_assert(NT == 1024, "the on-chip bounds assume 1024-thread selection blocks");
+    static_assert(KVX_ONCHIP_TOTAL > 32 * NT, "streaming selection above the register-held keys");
+    if (ws == nullptr && n_total > 32 * NT) {  // keys streamed from memory at every pass
+        select_stream_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        return check_launch(what);
+    }
+    if (ws == nullptr) {
+        // keys per thread: the smallest power of two covering n_total (identity needs none)
+        if (n_total <= NT || n_total <= p.budget)
+            select_kernel<1, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        else if (n_total <= 2 * NT)
+            select_kernel<2, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        else if (n_total <= 4 * NT)
+            select_kernel<4, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        else if (n_total <= 8 * NT)
+            select_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        else if (n_total <= 16 * NT)
+            select_kernel<16, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        else
+            select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        return check_launch(what);
+    }
+    const int W = (int)((n_total + MB_ROWS - 1) / MB_ROWS);
+    if (G * W > INT32_MAX) return set_error(KVX_ERANGE, "%s: grid too large", what);
+    const MbArgs args{s_kept, s_new, a, b, bud, ns, rc2, kl, W, ws};
+    mb_init_kernel<<<grid, 256, 0, st>>>(ws, W, bud);  // clears the histograms and state it reuses
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        mb_hist_kernel<<<(uint32_t)(G * W), MB_NT, 0, st>>>(args, shift);
+        mb_pick_kernel<<<grid, 64, 0, st>>>(ws, W, shift);
+    }
+    mb_count_kernel<<<(uint32_t)(G * W), MB_NT, 0, st>>>(args);
+    mb_write_kernel<<<(uint32_t)(G * W), MB_NT, 0, st>>>(args, keep_idx);
+    return check_launch(what);
+}
+
+// Bytes of device workspace the multi-block selection needs (0 on chip).
+int64_t select_workspace_bytes(int64_t G, int64_t n_total, int64_t budget) {
+    if (n_total <= KVX_ONCHIP_TOTAL || n_total <= budget) return 0;
+    const int64_t W = (n_total + MB_ROWS - 1) / MB_ROWS;
+    return G * (int64_t)mb_words((int)W) * 4;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t *g_scratch_ptr[kMaxDevices];  // per device, looked up on its first use
+
+// Device address of `scratch` on the current device (the one `stream` must
+// belong to), looked up once per device with that device current.
+int scratch_address(void *stream, uint32_t **out, const char *what) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return set_error(KVX_EDEVICE, "%s: no usable current device (%d)", what, dev);
+    if (stream != nullptr) {
+        hipDevice_t sd = -1;
+        if (hipStreamGetDevice((hipStream_t)stream, &sd) != hipSuccess)
+            return set_error(KVX_EINVAL, "%s: not a valid stream", what);
+        if (sd != dev)
+            return set_error(KVX_EINVAL, "%s: the stream belongs to device %d but device %d is current", what,
+                             (int)sd, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return set_error(KVX_EDEVICE, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", what, dev,
+                             hipGetErrorString(e));
+        g_scratch_ptr[dev] = (uint32_t *)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVX_OK;
+}
+
 }  // namespace
 }  // namespace kvx
 
@@ -995,13 +1086,6 @@ KVX_API int qf_score_keys(const void *k_new, kvx_shape shape, int64_t S, int32_t
     });
 }
 
-// Bytes of device workspace the multi-block selection needs (0 on chip).
-static int64_t select_workspace_bytes(int64_t G, int64_t n_total, int64_t budget) {
-    if (n_total <= KVX_ONCHIP_TOTAL || n_total <= budget) return 0;
-    const int64_t W = (n_total + MB_ROWS - 1) / MB_ROWS;
-    return G * (int64_t)mb_words((int)W) * 4;
-}
-
 KVX_API int kv_evict_workspace_size(kvx_shape shape, int64_t n_kept, int64_t S, kvx_evict_params p,
                                     size_t *bytes) {
     clear_error();
@@ -1028,45 +1112,30 @@ KVX_API int kv_evict_topk(const float *s_kept, const float *s_new, kvx_shape sha
     if (need > 0 && (ws == nullptr || (int64_t)ws_bytes < need))
         return set_error(KVX_EINVAL, "kv_evict_topk: n_total %lld needs a workspace of %lld bytes (got %zu)",
                          (long long)n_total, (long long)need, ws ? ws_bytes : (size_t)0);
-    hipStream_t st = (hipStream_t)stream;
-    const int a = (int)n_kept, b = (int)S, bud = (int)p.budget, ns = (int)p.n_sink, rc2 = (int)p.recent;
-    const int kl = p.keep == KVX_KEEP_LOW;
-    const uint32_t grid = (uint32_t)G;
-    constexpr int NT = KVX_SELECT_NT;
-    static_assert(NT == 1024, "the on-chip bounds assume 1024-thread selection blocks");
-    static_assert(KVX_ONCHIP_TOTAL > 32 * NT, "streaming selection above the register-held keys");
-    if (need == 0 && n_total > 32 * NT) {  // keys streamed from memory at every pass
-        select_stream_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-        return check_launch("kv_evict_topk");
-    }
-    if (need == 0) {
-        // keys per thread: the smallest power of two covering n_total (identity needs none)
-        if (n_total <= NT || n_total <= p.budget)
-            select_kernel<1, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-        else if (n_total <= 2 * NT)
-            select_kernel<2, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-        else if (n_total <= 4 * NT)
-            select_kernel<4, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-        else if (n_total <= 8 * NT)
-            select_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-        else if (n_total <= 16 * NT)
-            select_kernel<16, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-        else
-            select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
-        return check_launch("kv_evict_topk");
-    }
-    const int W = (int)((n_total + MB_ROWS - 1) / MB_ROWS);
-    if (G * W > INT32_MAX) return set_error(KVX_ERANGE, "kv_evict_topk: grid too large");
-    const MbArgs args{s_kept, s_new, a, b, bud, ns, rc2, kl, W, (uint32_t *)ws};
-    mb_init_kernel<<<grid, 256, 0, st>>>((uint32_t *)ws, W, bud);
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        mb_hist_kernel<<<(uint32_t)(G * W), MB_NT, 0, st>>>(args, shift);
-        mb_pick_kernel<<<grid, 64, 0, st>>>((uint32_t *)ws, W, shift);
-    }
-    mb_count_kernel<<<(uint32_t)(G * W), MB_NT, 0, st>>>(args);
-    mb_write_kernel<<<(uint32_t)(G * W), MB_NT, 0, st>>>(args, keep_idx);
-    return check_launch("kv_evict_topk");
+    return launch_select(s_kept, s_new, G, n_kept, S, p, keep_idx, need > 0 ? (uint32_t *)ws : nullptr,
+                         (hipStream_t)stream, "kv_evict_topk");
+}
+
+KVX_API int kv_evict_topk_noalloc(const float *s_kept, const float *s_new, kvx_shape shape, int64_t n_kept,
+                                  int64_t S, kvx_evict_params p, int32_t *keep_idx, void *stream) {
+    clear_error();
+    int64_t G = 0;
+    int rc = validate_select_sizes(shape, n_kept, S, p, &G);
+    if (rc) return rc;
+    const int64_t n_total = n_kept + S;
+    if (G == 0 || n_total == 0) return KVX_OK;
+    if (!keep_idx || (n_kept > 0 && !s_kept) || (S > 0 && !s_new))
+        return set_error(KVX_EINVAL, "kv_evict_topk_noalloc: NULL buffer");
+    const int64_t need = select_workspace_bytes(G, n_total, p.budget);
+    if (need > KVX_NOALLOC_SCRATCH_BYTES)
+        return set_error(KVX_ERANGE,
+                         "kv_evict_topk_noalloc: %lld groups selecting over %lld rows need %lld bytes of scratch; "
+                         "the static scratch holds %d (use kv_evict_topk with a workspace)",
+                         (long long)G, (long long)n_total, (long long)need, KVX_NOALLOC_SCRATCH_BYTES);
+    uint32_t *scr = nullptr;
+    if (need > 0 && (rc = scratch_address(stream, &scr, "kv_evict_topk_noalloc"))) return rc;
+    return launch_select(s_kept, s_new, G, n_kept, S, p, keep_idx, scr, (hipStream_t)stream,
+                         "kv_evict_topk_noalloc");
 }
 
 KVX_API int kv_compact_gather(const void *k_kept, const void *v_kept, const float *s_kept,
