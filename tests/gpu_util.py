@@ -98,3 +98,71 @@ def assert_state_invariants(cache, tokens: int, recent: int = 0) -> None:
     if recent and tokens > cache.budget:
         want = torch.arange(tokens - recent, tokens, device=p.device, dtype=p.dtype)
         assert bool((p[:, n - recent:] == want).all()), "the recent window must survive"
+
+
+# --------------------------------------------------------------------------- whole-workload helpers
+
+
+def host_rows(t, groups, dtype: str) -> np.ndarray:
+    """Host copy of t[groups] (one gather on the device, one transfer)."""
+    import torch
+    idx = torch.as_tensor(list(groups), dtype=torch.long, device=t.device)
+    return synth.torch_to_host(t.index_select(0, idx), dtype)
+
+
+def gpu_state_arrays(cache, groups):
+    """Host copies (k, v, s, pos) [len(groups), n_kept, ...] of the listed groups."""
+    import torch
+    k, v, s, p = cache.kept()
+    idx = torch.as_tensor(list(groups), dtype=torch.long, device=p.device)
+    return (synth.torch_to_host(k.index_select(0, idx), cache.dtype_name),
+            synth.torch_to_host(v.index_select(0, idx), cache.dtype_name),
+            s.index_select(0, idx).cpu().numpy(), p.index_select(0, idx).cpu().numpy())
+
+
+def assert_states_equal(state, ocache: oracle.OracleCache, groups, what: str = "") -> None:
+    """Bit-for-bit equality of the GPU state of `groups` (gpu_state_arrays)
+    with the oracle cache whose group i is groups[i]."""
+    k, v, s, p = state
+    n = p.shape[1]
+    assert np.all(ocache.n == n), "%s: kept counts differ (GPU %d, oracle %s)" % (what, n, np.unique(ocache.n))
+    pairs = (("positions", p, ocache.pos[:, :n]),
+             ("stored scores", s.view(np.uint32), ocache.s[:, :n].view(np.uint32)),
+             ("K bytes", k, ocache.k[:, :n]), ("V bytes", v, ocache.v[:, :n]))
+    for name, a, b in pairs:
+        if not np.array_equal(a, b):
+            same = np.all((a == b).reshape(len(groups), -1), axis=1)
+            bad = np.flatnonzero(~same)
+            raise AssertionError("%s: %s differ in %d of %d groups (first: group %d)" % (
+                what, name, bad.size, len(groups), list(groups)[bad[0]]))
+
+
+def oracle_scores(K: np.ndarray, dtype: str, mode: str, f=None, sign: int = 1) -> np.ndarray:
+    """The oracle's scores [n_groups, S] of K [n_groups, S, D] (f: [n_groups, D])."""
+    ng, S, Dd = K.shape
+    if mode == "l2":
+        return oracle.score(K.reshape(ng * S, Dd), "l2", None, 1, dtype).reshape(ng, S)
+    return np.stack([oracle.score(K[i], mode, f[i], sign, dtype) for i in range(ng)])
+
+
+def score_scales(K: np.ndarray, dtype: str, mode: str, s_ref: np.ndarray, f=None) -> np.ndarray:
+    """Error scale [n_groups, S] of every row: the norm itself for L2 (the
+    oracle's score), sum_d |k_d f_d| = |k| . |f| for projection."""
+    if mode == "l2":
+        return s_ref.astype(np.float64)
+    out = np.empty(K.shape[:2], dtype=np.float64)
+    for i in range(K.shape[0]):
+        out[i] = np.abs(widen(K[i], dtype)) @ np.abs(np.asarray(f[i], dtype=np.float64))
+    return out
+
+
+def certify_near_ties_pos(gpu_pos: np.ndarray, ref_pos: np.ndarray, s_ref: np.ndarray, tol: np.ndarray) -> int:
+    """certify_near_ties on arrays indexed by position (s_ref[pos], tol[pos])."""
+    a = np.setdiff1d(gpu_pos, ref_pos)
+    b = np.setdiff1d(ref_pos, gpu_pos)
+    assert a.size == b.size, "kept sets differ in size"
+    if a.size:
+        gap = np.abs(s_ref[a].astype(np.float64)[:, None] - s_ref[b].astype(np.float64)[None, :])
+        bound = tol[a][:, None] + tol[b][None, :]
+        assert np.all(gap <= bound), "kept positions differ by more than a near-tie: %s vs %s" % (a[:8], b[:8])
+    return int(a.size)
