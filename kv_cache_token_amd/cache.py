@@ -267,6 +267,7 @@ class EvictingCache:
                                        self.stream, prepare=prepare, cache_keys=self._cache_keys(S)))
         k, v, s, p = self._bufs[self._cur]
         nk, pos_base = self.n_kept, self.tokens_seen
+        ws = None
         if S == 1:
             calls.append(api.kv_evict_one_inplace(k, v, s, p, k_new, v_new, s_new, pos_base, self.shape, nk,
                                                   self.params, self.stream, prepare=prepare))
@@ -274,8 +275,9 @@ class EvictingCache:
             calls.append(api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, None, self.shape, nk, S,
                                                self.params, k, v, s, p, self.stream, prepare=prepare))
         else:
-            calls.append(api.kv_evict_topk(s, s_new, self.shape, nk, S, self.params, self.keep_idx,
-                                           self._workspace(nk, S), self.stream, prepare=prepare))
+            ws = self._workspace(nk, S)
+            calls.append(api.kv_evict_topk(s, s_new, self.shape, nk, S, self.params, self.keep_idx, ws,
+                                           self.stream, prepare=prepare))
             ko, vo, so, po = self._bufs[1 - self._cur]
             calls.append(api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, self.keep_idx,
                                                self.shape, nk, S, self.params, ko, vo, so, po, self.stream,
@@ -283,7 +285,9 @@ class EvictingCache:
             self._cur = 1 - self._cur
         self.n_kept = min(nk + S, self.budget)
         self.tokens_seen += S
-        return calls, (k_new, v_new, s_new)
+        # every tensor a prepared call points at: a later step may replace the
+        # workspace, and set_filters the filters, while a plan still uses them
+        return calls, (k_new, v_new, s_new, ws, self.filters)
 
     def plan(self, blocks, keep_state: bool = False) -> "StreamPlan":
         """Validate and record, once, the library calls that absorb `blocks`
@@ -291,30 +295,46 @@ class EvictingCache:
         keep_state, into the cache as it stands (the caller then restores the
         buffers before each replay).  The plan replays the calls with no
         per-call marshalling (or inside a captured HIP graph) and keeps the
-        tensors it points at alive.  The cache's bookkeeping is left at the
-        plan's starting state.  A stream that starts a key-SVD fallback cache
-        records the passthrough and the estimate as well; the filters are then
-        frozen to a buffer the plan writes when it runs (StreamPlan.check reads
-        the estimate's status)."""
+        tensors it points at alive (workspaces and filters included, even if
+        a later call replaces the cache's own).  The cache's bookkeeping is left
+        at the plan's starting state, and each run leaves it at the plan's final
+        state.  A stream that starts a key-SVD fallback cache records the
+        passthrough and the estimate as well; the filters are frozen to a
+        buffer the plan writes when it runs, and the cache points at that
+        buffer only once a run has been enqueued (StreamPlan.check reads the
+        estimate's status)."""
         start = (self.n_kept, self.tokens_seen, self._cur) if keep_state else (0, 0, 0)
+        start_aux = self._aux_state(None if not keep_state else self._held)
         self.n_kept, self.tokens_seen, self._cur = start
-        if not keep_state:
-            self._held = None
+        self._set_aux(start_aux)
         calls, keep = [], []
         for k, v in blocks:
             c, refs = self._step(k, v, prepare=True)
             calls += c
             keep.append(refs)
         final = (self.n_kept, self.tokens_seen, self._cur)
+        final_aux = self._aux_state(self._held)
+        keep.append(final_aux)
         self.n_kept, self.tokens_seen, self._cur = start
-        return StreamPlan(self, calls, start, final, keep)
+        self._set_aux(start_aux)
+        return StreamPlan(self, calls, start, final, keep, start_aux, final_aux)
+
+    def _aux_state(self, held):
+        """What a plan's calls change besides the counters: the frozen filters
+        (the fallback freezes them into a buffer the plan writes), the shape
+        they are read with, the estimate's status and the held rows."""
+        return (self.filters, self.score_shape, self.calib_status, held)
+
+    def _set_aux(self, aux) -> None:
+        self.filters, self.score_shape, self.calib_status, self._held = aux
 
 
 class StreamPlan:
     """Prepared library calls of a whole block stream (see EvictingCache.plan)."""
 
-    def __init__(self, cache: EvictingCache, calls, start, final, keepalive):
+    def __init__(self, cache: EvictingCache, calls, start, final, keepalive, start_aux, final_aux):
         self.cache, self.calls, self.start, self.final, self._keep = cache, calls, start, final, keepalive
+        self.start_aux, self.final_aux = start_aux, final_aux
 
     def check(self) -> None:
         """After run(): wait and raise if a fallback estimate the plan made failed."""
@@ -329,6 +349,7 @@ class StreamPlan:
         with when in ("before", "after") is called around each call."""
         c = self.cache
         c.n_kept, c.tokens_seen, c._cur = self.start
+        c._set_aux(self.start_aux)
         for i, (f, args) in enumerate(self.calls):
             if hook:
                 hook(i, f.__name__, "before")
@@ -339,3 +360,4 @@ class StreamPlan:
             if hook:
                 hook(i, f.__name__, "after")
         c.n_kept, c.tokens_seen, c._cur = self.final
+        c._set_aux(self.final_aux)
