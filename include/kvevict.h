@@ -192,6 +192,27 @@ KVX_API int kv_evict_topk_noalloc(const float *s_kept, const float *s_new, kvx_s
                                   int64_t S, kvx_evict_params p, int32_t *keep_idx, void *stream);
 
 /*
+ * Checked build.  A library compiled with -DKVX_CHECK (libkvevict_check.so)
+ * verifies the index lists of the selection and the compaction as it runs:
+ * the selection keeps exactly min(n_total, budget) rows and writes every one
+ * to a slot below the budget; every keep_idx entry the compaction reads lies
+ * in [0, n_kept + S) and is above the one before it.  The first violation is
+ * recorded in four device int32 words {code, group, row, value}; later ones
+ * are dropped.  Codes: */
+#define KVX_CHECK_SLOT 1  /* the selection produced a slot >= budget (value = slot)  */
+#define KVX_CHECK_RANGE 2 /* keep_idx[row] outside [0, n_kept + S) (value = index)   */
+#define KVX_CHECK_ORDER 3 /* keep_idx[row] <= keep_idx[row - 1] (value = index)      */
+#define KVX_CHECK_COUNT 4 /* the selection kept a number of rows != budget (value)   */
+/*
+ * kvx_check_status_word -- where the checked build records violations: device
+ * memory of 4 int32 that the caller zeroes and reads after synchronising (the
+ * library never clears it; NULL stops the recording).  One setting per
+ * process, read at each launch.  The normal build does no checking and
+ * returns KVX_EINVAL for a non-NULL pointer.  Errors: KVX_EINVAL.
+ */
+KVX_API int kvx_check_status_word(int32_t *status);
+
+/*
  * kv_compact_gather -- step 4: copy the survivors in temporal order.
  *   *_kept   device cache buffers holding n_kept rows per group (capacity budget)
  *   k_new, v_new, s_new  device incoming rows [G, S, *]
@@ -206,6 +227,11 @@ KVX_API int kv_evict_topk_noalloc(const float *s_kept, const float *s_new, kvx_s
  * Aliasing: the outputs must not overlap the inputs, except that when
  * n_kept + S <= budget all four outputs may be the kept buffers themselves
  * (then the incoming rows are appended in place and nothing else moves).
+ * keep_idx is not validated by the normal build: an entry outside
+ * [0, n_kept + S) is read as row 0 (no access leaves the buffers, but the
+ * result is wrong and the call still returns KVX_OK), and a list that is not
+ * strictly ascending gives rows out of temporal order.  The checked build
+ * records both (kvx_check_status_word).
  * Errors: KVX_EINVAL (including a partial alias), KVX_ERANGE, KVX_EDEVICE.
  */
 KVX_API int kv_compact_gather(const void *k_kept, const void *v_kept, const float *s_kept,

@@ -10,7 +10,10 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvevict.so")
+# KVX_LIB names another build of the same library (the host-sanitizer build
+# under _build/asan/); by default the in-tree libkvevict.so.
+LIB_PATH = os.environ.get("KVX_LIB") or os.path.join(HERE, "libkvevict.so")
+CHECK_LIB_PATH = os.path.join(HERE, "libkvevict_check.so")   # built with -DKVX_CHECK
 
 KVX_OK, KVX_EINVAL, KVX_ERANGE, KVX_EDEVICE, KVX_EIO, KVX_EMISMATCH = 0, -1, -2, -3, -4, -5
 KVX_F32, KVX_BF16, KVX_F16 = 0, 1, 2
@@ -48,6 +51,8 @@ class KvxError(RuntimeError):
 
 
 _lib = None
+_loaded = {}      # path -> CDLL
+_use_checked = False
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _SIGS = {
@@ -73,27 +78,56 @@ _SIGS = {
     "qf_filters_from_queries_device": ([_vp, _i32, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i32, _vp],
                                        ctypes.c_int),
     "kvx_stats": ([KvxShape, _i64, _i64, _i32, ctypes.POINTER(KvxStats)], ctypes.c_int),
+    "kvx_check_status_word": ([_vp], ctypes.c_int),
 }
+KVX_CHECK_SLOT, KVX_CHECK_RANGE, KVX_CHECK_ORDER, KVX_CHECK_COUNT = 1, 2, 3, 4
 
 
-def lib():
-    """The loaded library (raises if it has not been built)."""
-    global _lib
-    if _lib is None:
+def _load(path: str):
+    if path not in _loaded:
         try:
             import torch  # noqa: F401  (binds the library to torch's HIP runtime)
         except ImportError:
             pass
-        if not os.path.exists(LIB_PATH):
-            raise ImportError("libkvevict.so is not built (expected at %s); run "
-                              "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
-        L = ctypes.CDLL(LIB_PATH)
+        if not os.path.exists(path):
+            raise ImportError("%s is not built (expected at %s); run "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`" % (os.path.basename(path), path))
+        L = ctypes.CDLL(path)
         for name, (args, res) in _SIGS.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = res
-        _lib = L
+        _loaded[path] = L
+    return _loaded[path]
+
+
+def lib():
+    """The library every binding call goes to (raises if it has not been
+    built): libkvevict.so, or its checked build inside ``checked()``."""
+    global _lib
+    if _use_checked:
+        return _load(CHECK_LIB_PATH)
+    if _lib is None:
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+class checked:
+    """Context manager: calls made (or prepared) inside go to the checked build
+    (libkvevict_check.so, -DKVX_CHECK), which records index-list violations in
+    the status words given to kvx_check_status_word."""
+
+    def __enter__(self):
+        global _use_checked
+        self._prev = _use_checked
+        _load(CHECK_LIB_PATH)
+        _use_checked = True
+        return _load(CHECK_LIB_PATH)
+
+    def __exit__(self, *exc):
+        global _use_checked
+        _use_checked = self._prev
+        return False
 
 
 def check(fn: str, rc: int) -> None:

@@ -224,6 +224,13 @@ def qf_filters_from_queries_device(q, H_kv: int, out, status, max_iter: int = 20
     return _dispatch("qf_filters_from_queries_device", args, prepare)
 
 
+def kvx_check_status_word(status) -> None:
+    """Checked build only: record index-list violations in `status` (a CUDA
+    int32 tensor of 4 words the caller zeroes; None stops the recording)."""
+    torch = _torch()
+    call("kvx_check_status_word", _dev(status, "status", torch.int32, 4, allow_none=True))
+
+
 # --------------------------------------------------------------------------- host
 
 

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -64,6 +65,30 @@ namespace {
 #ifndef KVX_SELECT_NT
 #define KVX_SELECT_NT 1024
 #endif
+
+// Checked build (-DKVX_CHECK): the selection and the compaction verify the
+// index lists they write and read, and record the first violation in the
+// caller's status words {code, group, row, value} (kvx_check_status_word);
+// later violations are dropped.  Every access stays clamped as in the normal
+// build, so a violation never makes a kernel leave its buffers.
+#ifdef KVX_CHECK
+constexpr bool kCheck = true;
+#else
+constexpr bool kCheck = false;
+#endif
+
+__device__ __forceinline__ void check_record(int32_t *chk, int code, int g, int row, int value) {
+    if (chk != nullptr && atomicCAS(chk, 0, code) == 0) {
+        chk[1] = g;
+        chk[2] = row;
+        chk[3] = value;
+    }
+}
+
+// Status words of the checked build (set by kvx_check_status_word; always
+// nullptr in the normal build, whose kernels do not check).
+std::atomic<int32_t *> g_check_word{nullptr};
+int32_t *check_word() { return kCheck ? g_check_word.load(std::memory_order_relaxed) : nullptr; }
 
 // Order-preserving map of a score to an unsigned key, "higher key = better".
 // keep_low ranks by -s.  -0 becomes +0 first so that the two tie.
@@ -330,7 +355,7 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 template <int M, int NT>
 __device__ __forceinline__ void write_kept(const uint32_t *key, int r0, int n_total, uint32_t tau, uint32_t quota,
                                            uint32_t base_gt, uint32_t base_eq, int32_t *out, int budget,
-                                           uint32_t *chunk, uint32_t *total = nullptr) {
+                                           uint32_t *chunk, uint32_t *total, int32_t *chk) {
     constexpr int NW = NT / 64, NCH = M * NW, CPL = (NCH + 63) / 64;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
 #pragma unroll
@@ -377,7 +402,10 @@ __device__ __forceinline__ void write_kept(const uint32_t *key, int r0, int n_to
             slot = gb + min(eb, quota);
         else if (eq && eb < quota)
             slot = gb + eb;
-        if (slot < (uint32_t)budget) out[slot] = r;
+        if (slot < (uint32_t)budget)
+            out[slot] = r;
+        else if constexpr (kCheck)
+            if (slot != 0xFFFFFFFFu) check_record(chk, KVX_CHECK_SLOT, (int)blockIdx.x, r, (int)slot);
     }
     __syncthreads();
 }
@@ -392,7 +420,8 @@ template <int M, int NT>
 __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_kept,
                                                       const float *__restrict__ s_new, int n_kept,
                                                       int S, int budget, int n_sink, int recent,
-                                                      int keep_low, int32_t *__restrict__ keep_idx) {
+                                                      int keep_low, int32_t *__restrict__ keep_idx,
+                                                      int32_t *chk) {
     constexpr int NW = NT / 64;
     static_assert(NW >= 2, "wave 1 clears the histograms while wave 0 scans");
     const int g = blockIdx.x;
@@ -407,7 +436,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
                        keep_low};
 
     __shared__ uint4 hist4[2][64];  // 256-bin histograms, two passes' worth
-    __shared__ uint32_t sel[3];
+    __shared__ uint32_t sel[3], tot;
     __shared__ uint32_t chunk[M * NW];
     uint32_t(*hist)[256] = reinterpret_cast<uint32_t(*)[256]>(hist4);
 
@@ -455,7 +484,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const float *__restrict__ s_
         tau = prefix;
         quota = krem;
     }
-    write_kept<M, NT>(key, 0, n_total, tau, quota, 0, 0, out, budget, chunk);
+    write_kept<M, NT>(key, 0, n_total, tau, quota, 0, 0, out, budget, chunk, &tot, chk);
+    if constexpr (kCheck) {  // exactly `budget` rows kept
+        const uint32_t kept = (tot >> 16) + min(tot & 0xFFFFu, quota);
+        if (t == 0 && kept != (uint32_t)budget) check_record(chk, KVX_CHECK_COUNT, g, -1, (int)kept);
+    }
 }
 
 // One workgroup of NT threads per group for n_total up to KVX_ONCHIP_TOTAL:
@@ -469,7 +502,8 @@ template <int MS, int NT>
 __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restrict__ s_kept,
                                                              const float *__restrict__ s_new, int n_kept,
                                                              int S, int budget, int n_sink, int recent,
-                                                             int keep_low, int32_t *__restrict__ keep_idx) {
+                                                             int keep_low, int32_t *__restrict__ keep_idx,
+                                                             int32_t *chk) {
     constexpr int NW = NT / 64, CHUNK = MS * NT;
     static_assert(NW >= 2, "wave 1 clears the histograms while wave 0 scans");
     static_assert(CHUNK < 65536, "per-chunk counts are packed in 16 bits");
@@ -530,7 +564,7 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
     const uint32_t tau = whole ? prefix - 1 : prefix, quota = whole ? 0u : krem;
     uint32_t base_gt = 0, base_eq = 0;
     auto write_chunk = [&](int r0) {
-        write_kept<MS, NT>(key, r0, n_total, tau, quota, base_gt, base_eq, out, budget, chunk, &tot);
+        write_kept<MS, NT>(key, r0, n_total, tau, quota, base_gt, base_eq, out, budget, chunk, &tot, chk);
         const uint32_t c = tot;  // written before write_kept's last barrier
         base_gt += c >> 16;
         base_eq += c & 0xFFFFu;
@@ -545,6 +579,10 @@ __global__ __launch_bounds__(NT) void select_stream_kernel(const float *__restri
         make_keys<MS, NT>(rows, r0 + CHUNK, sb, key);
         if (r0 + 2 * CHUNK < n_total) load_scores<MS, NT>(rows, r0 + 2 * CHUNK, sa);
         write_chunk(r0 + CHUNK);
+    }
+    if constexpr (kCheck) {  // exactly `budget` rows kept
+        const uint32_t kept = base_gt + min(base_eq, quota);
+        if (t == 0 && kept != (uint32_t)budget) check_record(chk, KVX_CHECK_COUNT, g, -1, (int)kept);
     }
 }
 
@@ -565,6 +603,7 @@ struct MbArgs {
     const float *s_kept, *s_new;
     int n_kept, S, budget, n_sink, recent, keep_low, W;
     uint32_t *ws;
+    int32_t *chk;
 };
 
 __device__ __forceinline__ SelRows mb_rows(const MbArgs &a, int g) {
@@ -663,7 +702,18 @@ __global__ __launch_bounds__(MB_NT) void mb_write_kernel(MbArgs a, int32_t *__re
     load_keys<MB_M, MB_NT>(rows, r0, key);
     __syncthreads();
     write_kept<MB_M, MB_NT>(key, r0, rows.n_total, ws[256], ws[258], base[0], base[1],
-                            keep_idx + (size_t)g * a.budget, a.budget, chunk);
+                            keep_idx + (size_t)g * a.budget, a.budget, chunk, nullptr, a.chk);
+    if constexpr (kCheck) {  // exactly `budget` rows kept, over all row blocks
+        if (blk == a.W - 1 && t == 0) {
+            uint32_t n_gt = 0, n_eq = 0;
+            for (int b = 0; b < a.W; ++b) {
+                n_gt += ws[260 + 2 * b];
+                n_eq += ws[260 + 2 * b + 1];
+            }
+            const uint32_t kept = n_gt + min(n_eq, ws[258]);
+            if (kept != (uint32_t)a.budget) check_record(a.chk, KVX_CHECK_COUNT, g, -1, (int)kept);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -679,7 +729,7 @@ __global__ __launch_bounds__(KVX_GATHER_BLOCK) void gather_kernel(
     const char *__restrict__ k_new, const char *__restrict__ v_new,
     const float *__restrict__ s_new, int32_t pos_base, const int32_t *__restrict__ keep_idx,
     int n_kept, int S, int budget, int j0, int n_out, int blocks_per_group, char *__restrict__ k_out,
-    char *__restrict__ v_out, float *__restrict__ s_out, int32_t *__restrict__ pos_out) {
+    char *__restrict__ v_out, float *__restrict__ s_out, int32_t *__restrict__ pos_out, int32_t *chk) {
     using R = Row<DT, HD>;
     constexpr int kRowsPerPass = KVX_GATHER_BLOCK / R::kLanes;
     const int g = blockIdx.x / blocks_per_group;
@@ -698,6 +748,11 @@ __global__ __launch_bounds__(KVX_GATHER_BLOCK) void gather_kernel(
         src[u] = -1;
         if (j < n_out) {
             int r = keep_idx ? keep_idx[cache_row0 + j] : j;
+            if constexpr (kCheck) {
+                if (part == 0 && (unsigned)r >= (unsigned)(n_kept + S)) check_record(chk, KVX_CHECK_RANGE, g, j, r);
+                if (part == 0 && keep_idx && j > 0 && keep_idx[cache_row0 + j - 1] >= r)
+                    check_record(chk, KVX_CHECK_ORDER, g, j, r);
+            }
             if ((unsigned)r >= (unsigned)(n_kept + S)) r = 0;  // keep a corrupt index in bounds
             src[u] = r;
             const size_t off = r < n_kept ? (cache_row0 + r) * R::kBytes
@@ -965,7 +1020,7 @@ int launch_gather(const void *k_kept, const void *v_kept, const float *s_kept, c
     gather_kernel<DT, HD, U><<<(uint32_t)blocks, KVX_GATHER_BLOCK, 0, st>>>(
         (const char *)k_kept, (const char *)v_kept, s_kept, pos_kept, (const char *)k_new,
         (const char *)v_new, s_new, pos_base, keep_idx, n_kept, S, budget, j0, n_out, bpg,
-        (char *)k_out, (char *)v_out, s_out, pos_out);
+        (char *)k_out, (char *)v_out, s_out, pos_out, check_word());
     return check_launch("kv_compact_gather");
 }
 
@@ -977,32 +1032,33 @@ int launch_select(const float *s_kept, const float *s_new, int64_t G, int64_t n_
     const int a = (int)n_kept, b = (int)S, bud = (int)p.budget, ns = (int)p.n_sink, rc2 = (int)p.recent;
     const int kl = p.keep == KVX_KEEP_LOW;
     const uint32_t grid = (uint32_t)G;
+    int32_t *chk = check_word();
     constexpr int NT = KVX_SELECT_NT;
     static_assert(NT == 1024, "the on-chip bounds assume 1024-thread selection blocks");
     static_assert(KVX_ONCHIP_TOTAL > 32 * NT, "streaming selection above the register-held keys");
     if (ws == nullptr && n_total > 32 * NT) {  // keys streamed from memory at every pass
-        select_stream_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+        select_stream_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
         return check_launch(what);
     }
     if (ws == nullptr) {
         // keys per thread: the smallest power of two covering n_total (identity needs none)
         if (n_total <= NT || n_total <= p.budget)
-            select_kernel<1, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+            select_kernel<1, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
         else if (n_total <= 2 * NT)
-            select_kernel<2, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+            select_kernel<2, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
         else if (n_total <= 4 * NT)
-            select_kernel<4, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+            select_kernel<4, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
         else if (n_total <= 8 * NT)
-            select_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+            select_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
         else if (n_total <= 16 * NT)
-            select_kernel<16, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+            select_kernel<16, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
         else
-            select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx);
+            select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
         return check_launch(what);
     }
     const int W = (int)((n_total + MB_ROWS - 1) / MB_ROWS);
     if (G * W > INT32_MAX) return set_error(KVX_ERANGE, "%s: grid too large", what);
-    const MbArgs args{s_kept, s_new, a, b, bud, ns, rc2, kl, W, ws};
+    const MbArgs args{s_kept, s_new, a, b, bud, ns, rc2, kl, W, ws, chk};
     mb_init_kernel<<<grid, 256, 0, st>>>(ws, W, bud);  // clears the histograms and state it reuses
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
@@ -1136,6 +1192,14 @@ KVX_API int kv_evict_topk_noalloc(const float *s_kept, const float *s_new, kvx_s
     if (need > 0 && (rc = scratch_address(stream, &scr, "kv_evict_topk_noalloc"))) return rc;
     return launch_select(s_kept, s_new, G, n_kept, S, p, keep_idx, scr, (hipStream_t)stream,
                          "kv_evict_topk_noalloc");
+}
+
+KVX_API int kvx_check_status_word(int32_t *status) {
+    clear_error();
+    if (!kCheck && status != nullptr)
+        return set_error(KVX_EINVAL, "kvx_check_status_word: this library was built without KVX_CHECK");
+    g_check_word.store(status, std::memory_order_relaxed);
+    return KVX_OK;
 }
 
 KVX_API int kv_compact_gather(const void *k_kept, const void *v_kept, const float *s_kept,

@@ -30,7 +30,9 @@ from . import calib  # noqa: F401  (re-exported)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvx_oracle.c")
-_LIB = os.path.join(_HERE, "libkvx_oracle.so")
+_BUILT = os.path.join(_HERE, "libkvx_oracle.so")
+# KVX_ORACLE_LIB names another build of the same source (the sanitizer build).
+_LIB = os.environ.get("KVX_ORACLE_LIB") or _BUILT
 _lib = None
 
 MODE_L2, MODE_PROJ = 0, 1
@@ -40,18 +42,18 @@ _DT = {"f32": DT_F32, "bf16": DT_BF16, "f16": DT_F16}
 
 def build(force: bool = True) -> str:
     """Compile the oracle's C source into a shared object next to it."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+    if force or not os.path.exists(_BUILT):
+        tmp = _BUILT + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
                                _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, _BUILT)
+    return _BUILT
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if not os.path.exists(_LIB) and _LIB == _BUILT:
             build()
         L = ctypes.CDLL(_LIB)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p

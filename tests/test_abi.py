@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -265,3 +265,38 @@ def test_missing_library_fails_loudly(tmp_path):
                                            str(tmp_path / "absent.so")))
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert "raised" in out.stdout and "not built" in out.stdout, out.stdout + out.stderr
+
+
+def test_checked_build_exports_the_same_abi_and_only_it_takes_a_status_word():
+    """libkvevict_check.so (-DKVX_CHECK) has every symbol of the header; the
+    normal build refuses a status word, the checked one records where it is
+    (nothing is launched either way)."""
+    names = declared_functions()
+    with _lib.checked() as L:
+        for n in names:
+            assert hasattr(L, n), n
+        assert L.kvx_check_status_word(FAKE) == 0
+        assert L.kvx_check_status_word(None) == 0
+    assert _lib.lib().kvx_check_status_word(FAKE) == -1
+    assert b"KVX_CHECK" in _lib.lib().kvx_last_error()
+    assert _lib.lib().kvx_check_status_word(None) == 0
+
+
+def test_library_path_follows_the_environment_override():
+    """KVX_LIB / KVX_ORACLE_LIB (the sanitizer run) name the libraries that are
+    loaded; without them the in-tree builds are."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from kv_cache_token_amd import _lib\n"
+            "import oracle\n"
+            "print(_lib.LIB_PATH); print(oracle._LIB)\n" % root)
+    env = dict(os.environ, KVX_LIB="/x/a.so", KVX_ORACLE_LIB="/x/b.so")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, env=env)
+    assert out.stdout.split() == ["/x/a.so", "/x/b.so"], out.stdout + out.stderr
+    env.pop("KVX_LIB")
+    env.pop("KVX_ORACLE_LIB")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, env=env)
+    assert out.stdout.split() == [os.path.join(root, "kv_cache_token_amd", "libkvevict.so"),
+                                  os.path.join(root, "oracle", "libkvx_oracle.so")]

@@ -1,0 +1,136 @@
+"""The checked build (libkvevict_check.so, -DKVX_CHECK): it records nothing on
+valid streams -- the chunked 32k prefill of all 224 groups with both scorers,
+compared with the oracle as in the full-size tests, and selections on both
+sides of each on-chip bound -- and it records a corrupt keep_idx handed to the
+compaction (an index out of range, two indices out of order), which the normal
+build clamps and copies without a word."""
+import numpy as np
+import pytest
+
+from kv_cache_token_amd import synth
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_token_amd import _lib
+    _lib.lib()
+    with _lib.checked():
+        pass   # the checked build must be there: a missing one is an error, not a skip
+
+
+def _status():
+    import torch
+    return torch.zeros(4, dtype=torch.int32, device="cuda")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("which", [0, 1], ids=["l2_keep_low", "qfilters_sign_minus"])
+def test_checked_build_is_silent_on_the_32k_prefill(which):
+    import torch
+    from kv_cache_token_amd import _lib, api
+    from tests.test_gpu_configs import _run
+    cfg = synth.CONFIGS[4]
+    st = _status()
+    with _lib.checked():
+        api.kvx_check_status_word(st)
+        try:
+            _run(cfg, cfg.scorers[which], check_every=1)
+            torch.cuda.synchronize()
+        finally:
+            api.kvx_check_status_word(None)
+    assert st.cpu().tolist() == [0, 0, 0, 0]
+
+
+@pytest.mark.parametrize("n_kept,S,budget", [(4096, 4096, 4096), (16384, 16385, 16384), (100000, 162145, 100000),
+                                             (150000, 150000, 150000)])
+def test_checked_build_is_silent_on_selections(n_kept, S, budget):
+    import torch
+    import oracle
+    from kv_cache_token_amd import _lib, api
+    G = 5
+    rng = np.random.default_rng(n_kept + S)
+    sk = torch.from_numpy((rng.integers(-50, 50, (G, budget)) / 4.0).astype(np.float32)).cuda()
+    sn = torch.from_numpy((rng.integers(-50, 50, (G, S)) / 4.0).astype(np.float32)).cuda()
+    shape = api.make_shape(1, 1, G, "bf16")
+    p = api.make_params(budget, 4, 7, "high")
+    st = _status()
+    out = torch.full((G, budget), -1, dtype=torch.int32, device="cuda")
+    need = api.kv_evict_workspace_size(shape, n_kept, S, p)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    with _lib.checked():
+        api.kvx_check_status_word(st)
+        try:
+            api.kv_evict_topk(sk, sn, shape, n_kept, S, p, out, ws)
+            torch.cuda.synchronize()
+        finally:
+            api.kvx_check_status_word(None)
+    assert st.cpu().tolist() == [0, 0, 0, 0]
+    s = np.concatenate([sk[G - 1, :n_kept].cpu().numpy(), sn[G - 1].cpu().numpy()])
+    assert np.array_equal(out[G - 1].cpu().numpy(), oracle.select(s, budget, 4, 7, "high").astype(np.int32))
+
+
+def _gather_inputs(G, n_kept, S, budget):
+    import torch
+    k_kept = synth.host_to_torch(synth.custom_keys((G, budget, D), 71, "bf16"), "bf16").cuda()
+    v_kept = synth.host_to_torch(synth.custom_keys((G, budget, D), 72, "bf16"), "bf16").cuda()
+    k_new = synth.host_to_torch(synth.custom_keys((G, S, D), 73, "bf16"), "bf16").cuda()
+    v_new = synth.host_to_torch(synth.custom_keys((G, S, D), 74, "bf16"), "bf16").cuda()
+    s_kept = torch.arange(G * budget, dtype=torch.float32, device="cuda").reshape(G, budget)
+    s_new = -torch.arange(G * S, dtype=torch.float32, device="cuda").reshape(G, S)
+    pos_kept = torch.arange(G * budget, dtype=torch.int32, device="cuda").reshape(G, budget)
+    return k_kept, v_kept, s_kept, pos_kept, k_new, v_new, s_new
+
+
+@pytest.mark.parametrize("kind", ["range", "order"])
+def test_corrupt_keep_idx_is_recorded_by_the_checked_build_only(kind):
+    import torch
+    from kv_cache_token_amd import _lib, api
+    G, n_kept, S, budget = 3, 64, 32, 64
+    ins = _gather_inputs(G, n_kept, S, budget)
+    idx = np.stack([np.sort(np.random.default_rng(g).choice(n_kept + S, budget, replace=False))
+                    for g in range(G)]).astype(np.int32)
+    bad_g, bad_j = 1, (budget - 1 if kind == "range" else 10)
+    if kind == "range":
+        idx[bad_g, bad_j] = 1000                 # read as row 0 (clamped), recorded by the checked build
+        want = [_lib.KVX_CHECK_RANGE, bad_g, bad_j, 1000]
+    else:
+        idx[bad_g, bad_j - 1], idx[bad_g, bad_j] = idx[bad_g, bad_j], idx[bad_g, bad_j - 1]
+        want = [_lib.KVX_CHECK_ORDER, bad_g, bad_j, int(idx[bad_g, bad_j])]
+    keep_idx = torch.from_numpy(idx).cuda()
+    shape = api.make_shape(1, 1, G, "bf16")
+    p = api.make_params(budget, 4, 0, "low")
+
+    def gather():
+        outs = (torch.empty((G, budget, D), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((G, budget, D), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((G, budget), dtype=torch.float32, device="cuda"),
+                torch.empty((G, budget), dtype=torch.int32, device="cuda"))
+        api.kv_compact_gather(*ins[:4], ins[4], ins[5], ins[6], 1000, keep_idx, shape, n_kept, S, p, *outs)
+        torch.cuda.synchronize()
+        return outs
+
+    # normal build: no checking (the status word is refused), the index is clamped
+    with pytest.raises(_lib.KvxError):
+        api.kvx_check_status_word(_status())
+    outs = gather()
+    if kind == "range":
+        assert torch.equal(outs[0][bad_g, bad_j].view(torch.int16), ins[0][bad_g, 0].view(torch.int16))
+        assert int(outs[3][bad_g, bad_j]) == int(ins[3][bad_g, 0])
+    # checked build: the same call records the violation and still returns KVX_OK
+    st = _status()
+    with _lib.checked():
+        api.kvx_check_status_word(st)
+        try:
+            outs_c = gather()
+        finally:
+            api.kvx_check_status_word(None)
+    assert st.cpu().tolist() == want
+    for a, b in zip(outs, outs_c):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
