@@ -31,7 +31,7 @@ namespace {
 
 // Tuning knobs (compile-time): rows in flight per lane and cache hints.
 #ifndef KVX_SCORE_U
-#define KVX_SCORE_U 4
+#define KVX_SCORE_U 2
 #endif
 #ifndef KVX_GATHER_U
 #define KVX_GATHER_U 1
@@ -64,6 +64,11 @@ namespace {
 #endif
 #ifndef KVX_SELECT_NT
 #define KVX_SELECT_NT 1024
+#endif
+// Threads of the register-held selection for groups of up to 32 keys per
+// thread at this block size (KVX_SELECT_NT above that).
+#ifndef KVX_SELECT_SMALL_NT
+#define KVX_SELECT_SMALL_NT 1024
 #endif
 
 // Checked build (-DKVX_CHECK): the selection and the compaction verify the
@@ -1024,6 +1029,31 @@ int launch_gather(const void *k_kept, const void *v_kept, const float *s_kept, c
     return check_launch("kv_compact_gather");
 }
 
+// One workgroup of NT threads per group with the keys in registers: M keys
+// per thread, the smallest power of two covering n_total (one when nothing is
+// evicted: the identity needs no keys).
+template <int NT>
+int select_in_registers(const float *s_kept, const float *s_new, int64_t G, int64_t n_kept, int64_t S,
+                        const kvx_evict_params &p, int32_t *keep_idx, int32_t *chk, hipStream_t st, const char *what) {
+    const int64_t n_total = n_kept + S;
+    const int a = (int)n_kept, b = (int)S, bud = (int)p.budget, ns = (int)p.n_sink, rc2 = (int)p.recent;
+    const int kl = p.keep == KVX_KEEP_LOW;
+    const uint32_t grid = (uint32_t)G;
+    if (n_total <= NT || n_total <= p.budget)
+        select_kernel<1, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
+    else if (n_total <= 2 * NT)
+        select_kernel<2, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
+    else if (n_total <= 4 * NT)
+        select_kernel<4, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
+    else if (n_total <= 8 * NT)
+        select_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
+    else if (n_total <= 16 * NT)
+        select_kernel<16, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
+    else
+        select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
+    return check_launch(what);
+}
+
 // Selection launches after validation.  `ws` is the multi-block selection's
 // workspace (nullptr when it selects on chip).
 int launch_select(const float *s_kept, const float *s_new, int64_t G, int64_t n_kept, int64_t S,
@@ -1041,20 +1071,11 @@ int launch_select(const float *s_kept, const float *s_new, int64_t G, int64_t n_
         return check_launch(what);
     }
     if (ws == nullptr) {
-        // keys per thread: the smallest power of two covering n_total (identity needs none)
-        if (n_total <= NT || n_total <= p.budget)
-            select_kernel<1, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
-        else if (n_total <= 2 * NT)
-            select_kernel<2, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
-        else if (n_total <= 4 * NT)
-            select_kernel<4, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
-        else if (n_total <= 8 * NT)
-            select_kernel<8, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
-        else if (n_total <= 16 * NT)
-            select_kernel<16, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
-        else
-            select_kernel<32, NT><<<grid, NT, 0, st>>>(s_kept, s_new, a, b, bud, ns, rc2, kl, keep_idx, chk);
-        return check_launch(what);
+        constexpr int NS = KVX_SELECT_SMALL_NT;
+        static_assert(NS >= 128 && NS <= NT && NT % NS == 0, "small selection blocks of 2 to 16 waves");
+        if (NS < NT && n_total <= 32 * NS)
+            return select_in_registers<NS>(s_kept, s_new, G, n_kept, S, p, keep_idx, chk, st, what);
+        return select_in_registers<NT>(s_kept, s_new, G, n_kept, S, p, keep_idx, chk, st, what);
     }
     const int W = (int)((n_total + MB_ROWS - 1) / MB_ROWS);
     if (G * W > INT32_MAX) return set_error(KVX_ERANGE, "%s: grid too large", what);
