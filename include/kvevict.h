@@ -139,9 +139,10 @@ KVX_API int qf_score_keys(const void *k_new, kvx_shape shape, int64_t S, int32_t
 
 /*
  * kv_evict_workspace_size -- bytes of device workspace kv_evict_topk needs for
- * these sizes: 0 when n_kept + S <= KVX_ONCHIP_TOTAL (one workgroup per group
- * selects: up to 32768 rows with every key in registers, beyond that reading
- * the scores again at each radix pass) or when nothing is evicted; otherwise
+ * these sizes (implementation-defined; the pages define no workspace): 0 when
+ * n_kept + S <= KVX_ONCHIP_TOTAL (one workgroup per group selects: up to
+ * 32768 rows with every key in registers, beyond that reading the scores
+ * again at each radix pass) or when nothing is evicted; otherwise
  * G * (260 + 2 * ceil(n_total / 16384)) * 4 bytes for the multi-block
  * selection's histograms, state and block counts.  The caller allocates it;
  * kv_evict_topk initialises it itself on the stream (no memset needed), and
@@ -243,7 +244,10 @@ KVX_API int kv_compact_gather(const void *k_kept, const void *v_kept, const floa
 
 /*
  * kv_evict_one_inplace -- steps 2-4 for a single incoming row (S = 1), done in
- * place on the cache buffers (decode).
+ * place on the cache buffers (decode): the argmin-then-shift pattern of the
+ * pages' other Metal eviction kernels (Q-Filters page, "Metal kernels"), with
+ * the ranking and protection of the general step (same page, "How it works"
+ * step 4).
  *   *_cache  device cache buffers [G, budget, *] with n_kept valid rows
  *   k_new, v_new  device [G, 1, D];  s_new device [G] (from qf_score_keys)
  *   pos_base position of the incoming row
