@@ -50,7 +50,10 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                mean launch times, the library's own device-copy rate and (c2,
                c4) the same step launched layer by layer; --no-extras skips the
                last two.  --streams / --split run independent caches
-               concurrently (the default line uses one stream).
+               concurrently (--streams 2 puts the two scorer runs of c4 side
+               by side).  The default line uses one stream, so that the timed
+               steps, the per-kernel pass behind the roofline and a kernel
+               trace of the same command all see each kernel running alone.
 """
 from __future__ import annotations
 
@@ -643,7 +646,7 @@ def per_layer_ms(torch, wl, steps):
         for l in range(cfg.L):
             f = wl.f_mu[l:l + 1] if sc.filt == "mu" else None
             c = EvictingCache(1, cfg.B, cfg.H, cfg.budget, cfg.n_sink, cfg.recent, keep, sc.mode, f, sc.sign,
-                              cfg.dtype, stream=st)
+                              cfg.dtype, stream=st, head_dim=cfg.D)
             plans.append(c.plan([(k[l * bh:(l + 1) * bh], v[l * bh:(l + 1) * bh]) for k, v in wl.blocks]))
     run = lambda: [p.run() for p in plans]  # noqa: E731
     n_calls = sum(len(p.calls) for p in plans)
@@ -763,7 +766,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2, 4),
-                    help="streams the step's independent caches are spread over")
+                    help="streams the step's independent caches are spread over (2: the two scorer runs of c4 "
+                         "side by side)")
     ap.add_argument("--split", type=int, default=1,
                     help="divide each run's groups by layer into this many independent caches")
     ap.add_argument("--cpu-groups", type=int, default=32, help="groups in the oracle's timed sample")
@@ -898,7 +902,7 @@ def main():
     }
     if args.workload == "c5":
         out["fallback_estimate"] = fallback_estimate_time(torch, wl)
-    if args.workload in ("c2", "c4") and args.streams == 1 and args.split == 1 and graph is None \
+    if args.workload in ("c2", "c4") and args.split == 1 and graph is None \
             and not args.no_extras:
         out["per_layer_ms_per_step"] = per_layer_ms(torch, wl, max(1, args.steps // 4))
     parity = cb = None
