@@ -1,7 +1,8 @@
 """CPU oracle for the query-free KV-cache eviction step -- TEST INFRASTRUCTURE.
 
-Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg
-import this package.  The product (``kv_cache_token_amd`` and its HIP library)
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s oracle leg (the
+parity check of its own run and the CPU baseline, both on bytes copied back
+from the device) import this package.  The product (``kv_cache_token_amd`` and its HIP library)
 never imports it, and the two share no code: the only common input is the
 seeded generator module ``kv_cache_token_amd.synth``, which holds none of the
 method's arithmetic.

@@ -1,7 +1,7 @@
 /*
  * CPU ORACLE for the query-free KV-cache eviction step -- TEST INFRASTRUCTURE.
  *
- * Only the test-suite, the smoke entry and the benchmark's CPU-baseline leg may
+ * Only the test-suite, the smoke entry and the benchmark's oracle leg may
  * load this file's library.  The product path (the HIP library and its Python
  * binding) never calls it and shares no code with it.
  *
