@@ -209,6 +209,84 @@ class EvictingCache:
     def stats(self) -> dict:
         return api.kvx_stats(self.shape, self.tokens_seen, self.n_kept, self.mode)
 
+    # -- checkpoint ----------------------------------------------------------
+    STATE_VERSION = 1
+
+    def _config(self) -> dict:
+        return {"L": self.L, "B": self.B, "H": self.H, "D": self.D, "dtype": self.dtype_name, "budget": self.budget,
+                "n_sink": self.n_sink, "recent": self.recent, "keep": self.keep, "mode": self.mode,
+                "sign": self.sign, "calib_tokens": self.calib_tokens, "calib_keys": self.calib_keys}
+
+    def save_state(self, path: str) -> None:
+        """Write the cache's state to an uncompressed .npz holding no pickled
+        objects: the kept rows of every group (K and V as their stored bytes,
+        stored scores, positions), the kept count and the true offset, the
+        frozen filters, and, while a key-SVD fallback cache is still
+        calibrating, the rows it holds.  A cache built with the same parameters
+        resumes the stream from it (load_state).  Waits for the device.
+        (Q-Filters page, "Calibrated": only the filters are saved there; the
+        cache state itself is a convenience of this library.)"""
+        import json
+        import torch
+        torch.cuda.synchronize(self.device)
+        meta = dict(self._config(), version=self.STATE_VERSION, n_kept=self.n_kept, tokens_seen=self.tokens_seen,
+                    calibrating=self.calibrating, per_group_filters=self.score_shape is not self.shape)
+        k, v, sc, p = self.kept()
+        out = {"meta": np.array(json.dumps(meta)), "k": _host_bits(k), "v": _host_bits(v),
+               "pos": p.cpu().numpy()}
+        if sc is not None:
+            out["s"] = sc.cpu().numpy()
+        if self.filters is not None:
+            out["filters"] = self.filters.cpu().numpy()
+        with open(path, "wb") as f:
+            np.savez(f, **out)
+
+    def load_state(self, path: str) -> None:
+        """Resume from a file written by save_state; the cache's parameters
+        (shape, element type, budget, protection, scorer) must match the
+        saved ones (ValueError otherwise).  The kept rows land in the first
+        buffer set; the call returns once they are on the device."""
+        import json
+        import torch
+        with np.load(path, allow_pickle=False) as z:
+            meta = json.loads(str(z["meta"]))
+            arrays = {name: z[name] for name in z.files if name != "meta"}
+        if meta.get("version") != self.STATE_VERSION:
+            raise ValueError("cache state version %r, expected %d" % (meta.get("version"), self.STATE_VERSION))
+        want = self._config()
+        diff = {k: (meta.get(k), v) for k, v in want.items() if meta.get(k) != v}
+        if diff:
+            raise ValueError("cache state was saved with other parameters: %s" % ", ".join(
+                "%s %r (this cache: %r)" % (k, a, b) for k, (a, b) in sorted(diff.items())))
+        n = int(meta["n_kept"])
+        td = api.torch_dtype(self.shape.dtype)
+        with torch.cuda.device(self.device):
+            if "filters" in arrays:
+                self.set_filters(torch.from_numpy(arrays["filters"]), per_group=bool(meta["per_group_filters"]))
+            else:
+                self.filters, self.score_shape = None, self.shape
+            k = _device_rows(arrays["k"], td, self.device)
+            v = _device_rows(arrays["v"], td, self.device)
+            p = torch.from_numpy(arrays["pos"]).to(self.device)
+            if meta["calibrating"]:
+                cap = self.calib_tokens - 1
+                self._held = (torch.empty((self.G, cap, self.D), dtype=td, device=self.device),
+                              torch.empty((self.G, cap, self.D), dtype=td, device=self.device),
+                              torch.empty((self.G, cap), dtype=torch.int32, device=self.device))
+                for dst, src in zip(self._held, (k, v, p)):
+                    dst[:, :n].copy_(src)
+            else:
+                self._held = None
+                self._cur = 0
+                bk, bv, bs, bp = self._bufs[0]
+                bk[:, :n].copy_(k)
+                bv[:, :n].copy_(v)
+                bs[:, :n].copy_(torch.from_numpy(arrays["s"]).to(self.device))
+                bp[:, :n].copy_(p)
+            torch.cuda.synchronize(self.device)   # the copies are done before any stream reads them
+        self.n_kept, self.tokens_seen = n, int(meta["tokens_seen"])
+        self.calib_status = None
+
     # -- the step ----------------------------------------------------------
     def _workspace(self, n_kept: int, S: int):
         """Device workspace the selection needs for this call (None when it
@@ -327,6 +405,23 @@ class EvictingCache:
 
     def _set_aux(self, aux) -> None:
         self.filters, self.score_shape, self.calib_status, self._held = aux
+
+
+def _host_bits(t) -> np.ndarray:
+    """Host copy of K/V rows as their stored bytes (uint16 for 16-bit types)."""
+    import torch
+    t = t.detach().contiguous()
+    if t.dtype == torch.float32:
+        return t.cpu().numpy()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _device_rows(a: np.ndarray, td, device):
+    """Device tensor of element type td from stored row bytes (_host_bits)."""
+    import torch
+    if a.dtype == np.float32:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(td)
 
 
 class StreamPlan:

@@ -1,0 +1,132 @@
+"""Cache checkpoints: a stream saved part way (EvictingCache.save_state) and
+resumed in a fresh cache (load_state) ends in exactly the state of the
+uninterrupted stream -- kept rows, K/V bytes, stored scores, positions, true
+offset -- for the L2 and projection scorers and for a key-SVD fallback cache
+saved while it still holds unscored rows and after its filters froze; a
+cache with other parameters refuses the file."""
+import numpy as np
+import pytest
+
+from kv_cache_token_amd import synth
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_token_amd import _lib
+    _lib.lib()
+
+
+def _blocks(G, sizes, seed, dtype="bf16"):
+    import torch
+    out = []
+    for c, S in enumerate(sizes):
+        k = synth.host_to_torch(synth.custom_keys((G, S, D), seed + 2 * c, dtype), dtype).cuda()
+        v = synth.host_to_torch(synth.custom_keys((G, S, D), seed + 2 * c + 1, dtype), dtype).cuda()
+        out.append((k, v))
+    return out
+
+
+def _aniso_blocks(G, sizes, seed):
+    rng = np.random.default_rng(seed)
+    mu = rng.standard_normal(D)
+    mu /= np.linalg.norm(mu)
+    n = sum(sizes)
+    K = (rng.uniform(0.5, 2.0, (G, n, 1)) * mu + 0.5 * rng.standard_normal((G, n, D))).astype(np.float32)
+    kt = synth.host_to_torch(synth.encode(K, "bf16"), "bf16").cuda()
+    out, a = [], 0
+    for S in sizes:
+        out.append((kt[:, a:a + S].contiguous(), kt[:, a:a + S].flip(1).contiguous()))
+        a += S
+    return out
+
+
+def _same(a, b):
+    import torch
+    assert a.offset == b.offset and a.n_kept == b.n_kept
+    for x, y in zip(a.kept(), b.kept()):
+        if x is None or y is None:
+            assert x is None and y is None
+            continue
+        xx = x.view(torch.int16) if x.dtype in (torch.bfloat16, torch.float16) else x
+        yy = y.view(torch.int16) if y.dtype in (torch.bfloat16, torch.float16) else y
+        assert torch.equal(xx, yy)
+
+
+CASES = [("l2", "low", 1, None, "bf16"), ("proj", "high", -1, "f", "bf16"), ("l2", "high", 1, None, "f32")]
+
+
+@pytest.mark.parametrize("mode,keep,sign,filt,dtype", CASES, ids=["l2_bf16", "proj_bf16", "l2_high_f32"])
+def test_resumed_stream_equals_the_uninterrupted_one(tmp_path, mode, keep, sign, filt, dtype):
+    import torch
+    from kv_cache_token_amd.cache import EvictingCache
+    G, budget = 12, 300
+    f = torch.from_numpy(np.random.default_rng(2).standard_normal((3, 4, D)).astype(np.float32)) if filt else None
+    blocks = _blocks(G, (256, 256, 100, 1, 1, 512, 1), 60, dtype)
+
+    def make():
+        return EvictingCache(3, 1, 4, budget, 4, 8, keep, mode, f, sign, dtype)
+    whole = make()
+    for k, v in blocks:
+        whole.update(k, v)
+    for cut in (2, 4):
+        first = make()
+        for k, v in blocks[:cut]:
+            first.update(k, v)
+        path = str(tmp_path / ("state%d.npz" % cut))
+        first.save_state(path)
+        resumed = make()
+        resumed.load_state(path)
+        _same(first, resumed)
+        for k, v in blocks[cut:]:
+            resumed.update(k, v)
+        torch.cuda.synchronize()
+        _same(whole, resumed)
+
+
+def test_fallback_cache_resumes_while_holding_rows_and_after_the_freeze(tmp_path):
+    import torch
+    from kv_cache_token_amd.cache import EvictingCache
+    G = 8
+    blocks = _aniso_blocks(G, (50, 50, 300, 64), 17)
+
+    def make():
+        return EvictingCache(2, 1, 4, 64, 4, 0, mode="proj", calib_tokens=128)
+    whole = make()
+    for k, v in blocks:
+        whole.update(k, v)
+    for cut in (2, 3):     # 100 rows held unscored / filters frozen
+        first = make()
+        for k, v in blocks[:cut]:
+            first.update(k, v)
+        path = str(tmp_path / ("fb%d.npz" % cut))
+        first.save_state(path)
+        resumed = make()
+        resumed.load_state(path)
+        assert resumed.calibrating == (cut == 2)
+        for k, v in blocks[cut:]:
+            resumed.update(k, v)
+        torch.cuda.synchronize()
+        _same(whole, resumed)
+        assert torch.equal(whole.filters, resumed.filters)
+
+
+def test_state_with_other_parameters_is_refused(tmp_path):
+    from kv_cache_token_amd.cache import EvictingCache
+    c = EvictingCache(1, 1, 4, 64, 4, 0, "low", "l2")
+    k, v = _blocks(4, (100,), 5)[0]
+    c.update(k, v)
+    path = str(tmp_path / "s.npz")
+    c.save_state(path)
+    for other in (dict(budget=128), dict(n_sink=2), dict(keep="high")):
+        kw = dict(L=1, B=1, H=4, budget=64, n_sink=4, recent=0, keep="low", mode="l2")
+        kw.update(other)
+        with pytest.raises(ValueError, match="other parameters"):
+            EvictingCache(**kw).load_state(path)
+    with np.load(path, allow_pickle=False) as z:
+        assert z["k"].dtype == np.uint16 and z["k"].shape == (4, 64, D) and z["pos"].dtype == np.int32
