@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from kv_cache_token_amd import synth
-from tests.gpu_util import TOL, assert_scores_close, assert_states_equal, gpu_state_arrays, host_rows, \
+from tests.gpu_util import assert_scores_close, assert_states_equal, gpu_state_arrays, host_rows, \
     oracle_scores, score_scales
 
 pytestmark = pytest.mark.gpu
