@@ -733,8 +733,8 @@ def variant_config(args):
     naming them ("" when none is given)."""
     import dataclasses
     from kv_cache_token_amd import synth
-    opts = {k: getattr(args, k) for k in ("dtype", "head_dim", "budget", "chunk", "tokens")
-            if getattr(args, k) is not None}
+    opts = {k: getattr(args, k, None) for k in ("dtype", "head_dim", "budget", "chunk", "tokens", "layers")
+            if getattr(args, k, None) is not None}
     if args.workload == "qcal" and not opts:
         return None, ""
     if opts and args.workload not in ("c2", "c4", "c5"):
@@ -752,10 +752,14 @@ def variant_config(args):
     if head_dim == 256 and any(sc.filt == "keysvd" for sc in cfg.scorers):
         log("the key-SVD fallback estimates filters on the device for head dims 64 and 128 only")
         sys.exit(2)
-    cfg = dataclasses.replace(cfg, dtype=opts.get("dtype", cfg.dtype), D=head_dim,
+    layers = opts.get("layers", cfg.L)
+    if layers < 1:
+        log("--layers must be positive")
+        sys.exit(2)
+    cfg = dataclasses.replace(cfg, dtype=opts.get("dtype", cfg.dtype), D=head_dim, L=layers,
                               budget=opts.get("budget", cfg.budget), chunks=(chunk,) * (tokens // chunk))
-    text = "variant: %s K/V, head_dim %d, budget %d, %d tokens per run in %d-token chunks" % (
-        cfg.dtype, cfg.D, cfg.budget, tokens, chunk)
+    text = "variant: %d layer%s, %s K/V, head_dim %d, budget %d, %d tokens per run in %d-token chunks" % (
+        cfg.L, "" if cfg.L == 1 else "s", cfg.dtype, cfg.D, cfg.budget, tokens, chunk)
     return cfg, text
 
 
@@ -790,6 +794,7 @@ def main():
     vg.add_argument("--budget", type=int, help="rows kept per group")
     vg.add_argument("--chunk", type=int, help="tokens per call")
     vg.add_argument("--tokens", type=int, help="tokens per run (a multiple of the chunk)")
+    vg.add_argument("--layers", type=int, help="layers (each with the workload's KV heads)")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py measures one GPU: the library has no multi-GPU path (each GPU would run the same "

@@ -60,9 +60,13 @@ def test_prefill_variants_resize_the_recipe_and_reach_the_oracle_leg():
     assert (cfg.dtype, cfg.D, cfg.budget, cfg.chunks) == ("f16", 64, 20000, (16384,) * 4)
     assert cfg.scorers == synth.CONFIGS[4].scorers and "f16" in text and "20000" in text
     same, text0 = bench.variant_config(types.SimpleNamespace(workload="c4", dtype=None, head_dim=None, budget=None,
-                                                             chunk=None, tokens=None))
+                                                             chunk=None, tokens=None, layers=None))
     assert same is synth.CONFIGS[4] and text0 == ""
-    for bad in (dict(ns, workload="c3"), dict(ns, tokens=1000), dict(ns, workload="c5", head_dim=256)):
+    one, text1 = bench.variant_config(types.SimpleNamespace(workload="c2", dtype=None, head_dim=None, budget=None,
+                                                            chunk=256, tokens=None, layers=1))
+    assert (one.L, one.H, one.G, one.chunks) == (1, 8, 8, (256,) * 16) and "1 layer," in text1
+    for bad in (dict(ns, workload="c3"), dict(ns, tokens=1000), dict(ns, workload="c5", head_dim=256),
+                dict(ns, layers=0)):
         with pytest.raises(SystemExit):
             bench.variant_config(types.SimpleNamespace(**bad))
     # the oracle leg runs the variant's own bytes (fp16 rows of 64 elements)
