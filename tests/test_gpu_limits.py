@@ -7,7 +7,6 @@ import numpy as np
 import pytest
 
 import oracle
-from kv_cache_token_amd import synth
 from tests.gpu_util import assert_states_equal, gpu_state_arrays, host_rows, say
 
 pytestmark = pytest.mark.gpu
