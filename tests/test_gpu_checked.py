@@ -1,9 +1,9 @@
 """The checked build (libkvevict_check.so, -DKVX_CHECK): it records nothing on
-valid streams -- the chunked 32k prefill of all 224 groups with both scorers,
-compared with the oracle as in the full-size tests, and selections on both
-sides of each on-chip bound -- and it records a corrupt keep_idx handed to the
-compaction (an index out of range, two indices out of order), which the normal
-build clamps and copies without a word."""
+valid streams -- the five workloads at full size, compared with the oracle as
+in the full-size tests, and selections on both sides of each on-chip bound --
+and it records a corrupt keep_idx handed to the compaction (an index out of
+range, two indices out of order), which the normal build clamps and copies
+without a word."""
 import numpy as np
 import pytest
 
@@ -29,18 +29,25 @@ def _status():
     return torch.zeros(4, dtype=torch.int32, device="cuda")
 
 
+WORKLOAD_RUNS = [(4, 0), (4, 1), (2, 0), (5, 0), (3, 0)]
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("which", [0, 1], ids=["l2_keep_low", "qfilters_sign_minus"])
-def test_checked_build_is_silent_on_the_32k_prefill(which):
+@pytest.mark.parametrize("cid,which", WORKLOAD_RUNS, ids=["c4_l2", "c4_qfilters_sign_minus", "c2", "c5", "c3"])
+def test_checked_build_is_silent_on_the_workloads(cid, which):
+    """The five workloads at full size through the checked build, compared
+    with the oracle as in the full-size tests (every group; for the decode
+    stream the first and the last sequence)."""
     import torch
     from kv_cache_token_amd import _lib, api
-    from tests.test_gpu_configs import _run
-    cfg = synth.CONFIGS[4]
+    from tests.test_gpu_configs import _run, _sequences
+    cfg = synth.CONFIGS[cid]
+    groups = _sequences(cfg, (0, cfg.B - 1)) if cid == 3 else None
     st = _status()
     with _lib.checked():
         api.kvx_check_status_word(st)
         try:
-            _run(cfg, cfg.scorers[which], check_every=1)
+            _run(cfg, cfg.scorers[which], groups, check_every=64 if cid == 3 else 1)
             torch.cuda.synchronize()
         finally:
             api.kvx_check_status_word(None)
