@@ -34,7 +34,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                scores it ranks) per launch over its mean duration from HIP
                events recorded on the launch stream around every call, in a
                second timed pass; the bytes the kernel itself moves and the
-               rocprofv3 counters' HBM traffic beside them
+               rocprofv3 counters' HBM traffic beside them.  (A call that
+               evicts nothing scores and appends in one pass, kv_score_append,
+               and has no compaction launch.)
   parity       the oracle's verdict on the sampled groups: an untimed pass
                copies back their input bytes and the GPU's scores of every
                call; the oracle replays its selection and compaction on those
@@ -248,7 +250,7 @@ def capture_pass(torch, wl):
             calls, st = [], {"blk": 0}
 
             def hook(i, name, when, c=c, loc=loc, blocks=blocks, calls=calls, st=st, l0=l0):
-                if when != "after" or name != "qf_score_keys":
+                if when != "after" or name not in ("qf_score_keys", "kv_score_append"):
                     return
                 b = st["blk"]
                 k, v = blocks[b]
@@ -287,11 +289,16 @@ def algorithmic_bytes(torch, wl):
 
         def hook(i, name, when, cache=cache, st=st):
             nonlocal total
+            if name in ("qf_score_keys", "kv_score_append") and when == "after":
+                st["S"] = cache.last_scores().shape[1]
             if name == "qf_score_keys":
-                if when == "after":
-                    st["S"] = cache.last_scores().shape[1]
                 return
             S, nk = st["S"], st["n_kept"]
+            if name == "kv_score_append":
+                if when == "after":   # nothing evicted: every incoming row appended
+                    total += G * (S * ROW + 4 * nk + S * (3 * ROW + 8))
+                    st["n_kept"] = nk + S
+                return
             if name == "kv_evict_one_inplace":
                 if when == "before":
                     torch.cuda.synchronize()

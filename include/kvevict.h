@@ -153,6 +153,30 @@ KVX_API int kv_evict_workspace_size(kvx_shape shape, int64_t n_kept, int64_t S,
                                     kvx_evict_params p, size_t *bytes);
 
 /*
+ * kv_score_append -- steps 1-4 of a call that evicts nothing (n_kept + S <=
+ * budget): every incoming row is kept (L2Norm page, "How it works"; Q-Filters
+ * page, "How it works" step 4: eviction only when over budget), so the rows
+ * are scored and appended in one pass and each key is read once.  The result
+ * is bit for bit that of qf_score_keys followed by the in-place
+ * kv_compact_gather: rows n_kept .. n_kept + S - 1 of every group receive the
+ * incoming K and V bytes, the score (same fixed-order float32 sum, -0 stored
+ * as +0) and the position pos_base + i.
+ *   k_new, v_new   device [G, S, D] of shape.dtype; must not be the cache buffers
+ *   mode, filters, sign   as qf_score_keys (KVX_SCORE_CACHE_KEYS is accepted
+ *                  and has no effect); shape describes the filters' layout as
+ *                  there, and the cache's groups are the same G
+ *   *_cache        device cache buffers [G, budget, *] with n_kept valid rows
+ *   s_new          device [G, S] float32 copy of the scores, or NULL
+ * Errors: KVX_EINVAL (n_kept + S > budget: such a call evicts and needs
+ * kv_evict_topk and kv_compact_gather; bad mode/sign, NULL, aliasing),
+ * KVX_ERANGE, KVX_EDEVICE.
+ */
+KVX_API int kv_score_append(const void *k_new, const void *v_new, kvx_shape shape, int64_t S, int32_t mode,
+                            const float *filters, int32_t sign, int64_t pos_base, int64_t n_kept,
+                            kvx_evict_params p, void *k_cache, void *v_cache, float *s_cache, int32_t *pos_cache,
+                            float *s_new, void *stream);
+
+/*
  * kv_evict_topk -- steps 2-3: which rows of the concatenation survive.
  *   s_kept   device [G, budget] stored scores of the n_kept kept rows
  *   s_new    device [G, S] scores of the incoming rows (from qf_score_keys)

@@ -60,6 +60,8 @@ _SIGS = {
     "kvx_abi_version": ([], ctypes.c_int),
     "qf_score_keys": ([_vp, KvxShape, _i64, _i32, _vp, _i32, _vp, _vp], ctypes.c_int),
     "kv_evict_workspace_size": ([KvxShape, _i64, _i64, KvxParams, ctypes.POINTER(_sz)], ctypes.c_int),
+    "kv_score_append": ([_vp, _vp, KvxShape, _i64, _i32, _vp, _i32, _i64, _i64, KvxParams, _vp, _vp, _vp, _vp,
+                         _vp, _vp], ctypes.c_int),
     "kv_evict_topk": ([_vp, _vp, KvxShape, _i64, _i64, KvxParams, _vp, _vp, _sz, _vp], ctypes.c_int),
     "kv_evict_topk_noalloc": ([_vp, _vp, KvxShape, _i64, _i64, KvxParams, _vp, _vp], ctypes.c_int),
     "kv_compact_gather": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, KvxShape, _i64, _i64, KvxParams,

@@ -116,6 +116,22 @@ def qf_score_keys(k_new, shape: KvxShape, S: int, mode, filters, sign: int, s_ne
     return _dispatch("qf_score_keys", (kp, shape, S, mf, fp, sign, sp, _stream(stream)), prepare)
 
 
+def kv_score_append(k_new, v_new, shape: KvxShape, S: int, mode, filters, sign: int, pos_base: int, n_kept: int,
+                    params: KvxParams, k_cache, v_cache, s_cache, pos_cache, s_new=None, stream=None,
+                    prepare: bool = False):
+    """Score the S incoming rows and append them after the n_kept kept rows in
+    one pass (a call that evicts nothing: n_kept + S <= budget)."""
+    torch = _torch()
+    G, m, td, cap, Dd = _G(shape), mode_code(mode), torch_dtype(shape.dtype), params.budget, shape.D
+    args = (_dev(k_new, "k_new", td, G * S * Dd), _dev(v_new, "v_new", td, G * S * Dd), shape, S, m,
+            _dev(filters, "filters", torch.float32, shape.L * shape.H * Dd, allow_none=(m == KVX_SCORE_L2)), sign,
+            pos_base, n_kept, params,
+            _dev(k_cache, "k_cache", td, G * cap * Dd), _dev(v_cache, "v_cache", td, G * cap * Dd),
+            _dev(s_cache, "s_cache", torch.float32, G * cap), _dev(pos_cache, "pos_cache", torch.int32, G * cap),
+            _dev(s_new, "s_new", torch.float32, G * S, allow_none=True), _stream(stream))
+    return _dispatch("kv_score_append", args, prepare)
+
+
 def kv_evict_workspace_size(shape: KvxShape, n_kept: int, S: int, params: KvxParams) -> int:
     n = ctypes.c_size_t(0)
     call("kv_evict_workspace_size", shape, n_kept, S, params, ctypes.byref(n))

@@ -5,7 +5,8 @@ evicts, a keep-index buffer and the incoming-score buffer), the kept-row count
 and the true offset (tokens seen, Q-Filters page, "RoPE positions had to be
 fixed first").  Each ``update`` is the query-free step of the pages
 (Q-Filters page and L2Norm page, "How it works"): score the incoming rows,
-select, compact; all arithmetic runs in the library's kernels on one stream.
+select, compact -- or, when the block evicts nothing, score and append in one
+pass; all arithmetic runs in the library's kernels on one stream.
 A projection cache built without filters runs the key-SVD fallback's lifecycle
 on the device (Q-Filters page, "How it works" step 2, "Key-SVD fallback"):
 rows are held unscored below calib_tokens, and the crossing block freezes one
@@ -301,14 +302,13 @@ class EvictingCache:
 
     def _cache_keys(self, S: int) -> bool:
         """Whether scoring should leave the block's keys in the last-level
-        cache: they must fit it, and the compaction must be expected to re-read
-        at least a quarter of them (every row when nothing is evicted; about
-        budget / n_total of them otherwise)."""
+        cache for the compaction of an evicting call: they must fit it, and the
+        compaction must be expected to re-read at least a quarter of them
+        (about budget / n_total of them)."""
         row = self.D * (4 if self.dtype_name == "f32" else 2)
         if self.G * S * row > 0.9 * LAST_LEVEL_CACHE_BYTES:
             return False
-        n_total = self.n_kept + S
-        return n_total <= self.budget or 4 * self.budget >= n_total
+        return 4 * self.budget >= self.n_kept + S
 
     def _scores(self, S: int):
         import torch
@@ -341,17 +341,22 @@ class EvictingCache:
                 return calls, (k_new, v_new) + self._held
             return self._crossing(k_new, v_new, S, prepare)
         s_new = self._scores(S)
-        calls.append(api.qf_score_keys(k_new, self.score_shape, S, self.mode, self.filters, self.sign, s_new,
-                                       self.stream, prepare=prepare, cache_keys=self._cache_keys(S)))
         k, v, s, p = self._bufs[self._cur]
         nk, pos_base = self.n_kept, self.tokens_seen
         ws = None
+        if S > 1 and nk + S <= self.budget:
+            # nothing is evicted: score and append in one pass (keys read once)
+            calls.append(api.kv_score_append(k_new, v_new, self.score_shape, S, self.mode, self.filters, self.sign,
+                                             pos_base, nk, self.params, k, v, s, p, s_new, self.stream,
+                                             prepare=prepare))
+            self.n_kept = nk + S
+            self.tokens_seen += S
+            return calls, (k_new, v_new, s_new, ws, self.filters)
+        calls.append(api.qf_score_keys(k_new, self.score_shape, S, self.mode, self.filters, self.sign, s_new,
+                                       self.stream, prepare=prepare, cache_keys=self._cache_keys(S)))
         if S == 1:
             calls.append(api.kv_evict_one_inplace(k, v, s, p, k_new, v_new, s_new, pos_base, self.shape, nk,
                                                   self.params, self.stream, prepare=prepare))
-        elif nk + S <= self.budget:
-            calls.append(api.kv_compact_gather(k, v, s, p, k_new, v_new, s_new, pos_base, None, self.shape, nk, S,
-                                               self.params, k, v, s, p, self.stream, prepare=prepare))
         else:
             ws = self._workspace(nk, S)
             calls.append(api.kv_evict_topk(s, s_new, self.shape, nk, S, self.params, self.keep_idx, ws,

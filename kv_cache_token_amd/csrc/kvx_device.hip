@@ -65,6 +65,14 @@ namespace {
 #ifndef KVX_SELECT_NT
 #define KVX_SELECT_NT 1024
 #endif
+// Score-and-append (calls that evict nothing): threads per block and rows in
+// flight per lane (1024 and 1 measured fastest: the copy dominates).
+#ifndef KVX_APPEND_BLOCK
+#define KVX_APPEND_BLOCK 1024
+#endif
+#ifndef KVX_APPEND_U
+#define KVX_APPEND_U 1
+#endif
 // Threads of the register-held selection for groups of up to 32 keys per
 // thread at this block size (KVX_SELECT_NT above that).
 #ifndef KVX_SELECT_SMALL_NT
@@ -722,6 +730,56 @@ __global__ __launch_bounds__(MB_NT) void mb_write_kernel(MbArgs a, int32_t *__re
 }
 
 // ---------------------------------------------------------------------------
+// Steps 1-4 of a call that evicts nothing: every incoming row is kept, so it
+// is scored and appended in the same pass and its key is read once.  A row is
+// kLanes lanes x 16 B of K and of V; each lane reduces its K slice exactly as
+// the scoring kernels do (same function, same order), so the stored score is
+// the one qf_score_keys gives.  Blocks are group-major tiles of incoming rows.
+// ---------------------------------------------------------------------------
+template <int DT, int HD, int MODE, int U>
+__global__ __launch_bounds__(KVX_APPEND_BLOCK) void score_append_kernel(
+    const char *__restrict__ k_new, const char *__restrict__ v_new, uint32_t S, uint32_t tiles, uint32_t BH,
+    uint32_t H, const float *__restrict__ filt, float sign, int32_t pos_base, uint32_t n_kept, uint32_t budget,
+    char *__restrict__ k_cache, char *__restrict__ v_cache, float *__restrict__ s_cache,
+    int32_t *__restrict__ pos_cache, float *__restrict__ s_new) {
+    using R = Row<DT, HD>;
+    constexpr int kRowsPerLoad = 64 / R::kLanes;
+    constexpr int kRowsPerWave = kRowsPerLoad * U;
+    const uint32_t g = blockIdx.x / tiles;
+    const uint32_t tile = blockIdx.x - g * tiles;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t sub = lane / R::kLanes, part = lane % R::kLanes;
+    const uint32_t r0 = tile * (KVX_APPEND_BLOCK / 64) * kRowsPerWave + (threadIdx.x >> 6) * kRowsPerWave + sub;
+    const size_t in0 = (size_t)g * S, out0 = (size_t)g * budget + n_kept;
+    float f[R::kElemsPerLane];
+    if constexpr (MODE == KVX_SCORE_PROJ) load_filter_slice<DT, HD>(filt, g / BH, g % H, H, part, f);
+    uint4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t r = r0 + u * kRowsPerLoad;
+        const size_t off = (in0 + r) * R::kBytes + part * 16;
+        kr[u] = r < S ? ld16<true>(k_new + off) : make_uint4(0, 0, 0, 0);
+        vr[u] = r < S ? ld16<true>(v_new + off) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t r = r0 + u * kRowsPerLoad;
+        const float acc = row_partial<DT, HD, MODE>(kr[u], f);
+        if (r < S) {
+            const size_t off = (out0 + r) * R::kBytes + part * 16;
+            st16<true>(k_cache + off, kr[u]);
+            st16<true>(v_cache + off, vr[u]);
+            if (part == 0) {
+                const float sc = finish_score(MODE, acc, sign);
+                s_cache[out0 + r] = sc;
+                pos_cache[out0 + r] = pos_base + (int32_t)r;
+                if (s_new) s_new[in0 + r] = sc;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Step 4: gather.  Output rows j in [j0, n_out) of every group; blocks are
 // numbered group-major.  Each row is kLanes lanes x 16 B for K and the same for
 // V; the lane with part == 0 also moves the score and the position.
@@ -1029,6 +1087,22 @@ int launch_gather(const void *k_kept, const void *v_kept, const float *s_kept, c
     return check_launch("kv_compact_gather");
 }
 
+template <int DT, int HD, int MODE>
+int launch_score_append(const void *k_new, const void *v_new, int64_t G, const kvx_shape &sh, int64_t S,
+                        const float *filters, float sign, int32_t pos_base, int64_t n_kept, int64_t budget,
+                        void *k_cache, void *v_cache, float *s_cache, int32_t *pos_cache, float *s_new,
+                        hipStream_t st) {
+    constexpr int U = KVX_APPEND_U;
+    constexpr int kRowsPerBlock = (KVX_APPEND_BLOCK / 64) * (64 / Row<DT, HD>::kLanes) * U;
+    const uint32_t tiles = (uint32_t)((S + kRowsPerBlock - 1) / kRowsPerBlock);
+    if ((int64_t)tiles * G > INT32_MAX) return set_error(KVX_ERANGE, "kv_score_append: grid too large");
+    score_append_kernel<DT, HD, MODE, U><<<(uint32_t)(tiles * G), KVX_APPEND_BLOCK, 0, st>>>(
+        (const char *)k_new, (const char *)v_new, (uint32_t)S, tiles, (uint32_t)(sh.B * sh.H), (uint32_t)sh.H,
+        filters, sign, pos_base, (uint32_t)n_kept, (uint32_t)budget, (char *)k_cache, (char *)v_cache, s_cache,
+        pos_cache, s_new);
+    return check_launch("kv_score_append");
+}
+
 // One workgroup of NT threads per group with the keys in registers: M keys
 // per thread, the smallest power of two covering n_total (one when nothing is
 // evicted: the identity needs no keys).
@@ -1221,6 +1295,48 @@ KVX_API int kvx_check_status_word(int32_t *status) {
         return set_error(KVX_EINVAL, "kvx_check_status_word: this library was built without KVX_CHECK");
     g_check_word.store(status, std::memory_order_relaxed);
     return KVX_OK;
+}
+
+KVX_API int kv_score_append(const void *k_new, const void *v_new, kvx_shape shape, int64_t S, int32_t mode,
+                            const float *filters, int32_t sign, int64_t pos_base, int64_t n_kept,
+                            kvx_evict_params p, void *k_cache, void *v_cache, float *s_cache, int32_t *pos_cache,
+                            float *s_new, void *stream) {
+    clear_error();
+    int64_t G = 0;
+    int rc = validate_select_sizes(shape, n_kept, S, p, &G);
+    if (rc) return rc;
+    mode &= ~KVX_SCORE_CACHE_KEYS;  // the keys are read once here either way
+    if (mode != KVX_SCORE_L2 && mode != KVX_SCORE_PROJ)
+        return set_error(KVX_EINVAL, "kv_score_append: mode must be KVX_SCORE_L2 or KVX_SCORE_PROJ (got %d)",
+                         (int)mode);
+    if (mode == KVX_SCORE_PROJ && sign != 1 && sign != -1)
+        return set_error(KVX_EINVAL, "kv_score_append: sign must be +1 or -1 (got %d)", (int)sign);
+    if (mode == KVX_SCORE_PROJ && filters == nullptr)
+        return set_error(KVX_EINVAL, "kv_score_append: projection needs filters");
+    if (n_kept + S > p.budget)
+        return set_error(KVX_EINVAL,
+                         "kv_score_append: n_kept + S = %lld exceeds the budget %lld (a call that evicts needs "
+                         "kv_evict_topk and kv_compact_gather)", (long long)(n_kept + S), (long long)p.budget);
+    if (pos_base < 0 || pos_base + S > INT32_MAX)
+        return set_error(KVX_ERANGE, "kv_score_append: positions must fit int32 (pos_base %lld, S %lld)",
+                         (long long)pos_base, (long long)S);
+    if (G == 0 || S == 0) return KVX_OK;
+    if (G * S >= ((int64_t)1 << 31)) return set_error(KVX_ERANGE, "kv_score_append: G*S must be below 2^31");
+    if (!k_new || !v_new || !k_cache || !v_cache || !s_cache || !pos_cache)
+        return set_error(KVX_EINVAL, "kv_score_append: NULL buffer");
+    if (k_new == k_cache || v_new == v_cache || k_new == v_cache || v_new == k_cache)
+        return set_error(KVX_EINVAL, "kv_score_append: the incoming rows must not be the cache buffers");
+    hipStream_t st = (hipStream_t)stream;
+    return dispatch_row(shape, false, [&](auto dt, auto hd) {
+        constexpr int DT = decltype(dt)::value, HD = decltype(hd)::value;
+        if (mode == KVX_SCORE_L2)
+            return launch_score_append<DT, HD, KVX_SCORE_L2>(k_new, v_new, G, shape, S, filters, 1.0f,
+                                                             (int32_t)pos_base, n_kept, p.budget, k_cache, v_cache,
+                                                             s_cache, pos_cache, s_new, st);
+        return launch_score_append<DT, HD, KVX_SCORE_PROJ>(k_new, v_new, G, shape, S, filters, (float)sign,
+                                                           (int32_t)pos_base, n_kept, p.budget, k_cache, v_cache,
+                                                           s_cache, pos_cache, s_new, st);
+    });
 }
 
 KVX_API int kv_compact_gather(const void *k_kept, const void *v_kept, const float *s_kept,

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     L = _lib.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -40,6 +40,7 @@ def _rc(fn, *args):
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+C1, C2, C3, C4 = (ctypes.c_void_p(0x1000 * (i + 2)) for i in range(4))
 
 
 def test_validation_rejects_bad_calls_without_launching():
@@ -94,6 +95,13 @@ def test_validation_rejects_bad_calls_without_launching():
         ("qf_filters_from_queries_device", (FAKE, 1, 2, 6, 100, 256, 2, FAKE, FAKE, 100, None), -2),
         ("qf_filters_from_queries_device", (FAKE, 1, 2, 6, 100, 128, 2, FAKE, FAKE, 0, None), -1),
         ("qf_filters_from_queries_device", (None, 1, 2, 6, 100, 128, 2, FAKE, FAKE, 100, None), -1),
+        ("kv_score_append", (FAKE, FAKE, sh, 10, 0, None, 1, 0, 60, ok, C1, C2, C3, C4, None, None), -1),  # evicts
+        ("kv_score_append", (FAKE, FAKE, sh, 10, 1, None, 1, 0, 0, ok, C1, C2, C3, C4, None, None), -1),   # no filter
+        ("kv_score_append", (FAKE, FAKE, sh, 10, 1, FAKE, 3, 0, 0, ok, C1, C2, C3, C4, None, None), -1),   # sign
+        ("kv_score_append", (FAKE, FAKE, sh, 10, 7, FAKE, 1, 0, 0, ok, C1, C2, C3, C4, None, None), -1),   # mode
+        ("kv_score_append", (FAKE, FAKE, sh, 10, 0, None, 1, 0, 0, ok, FAKE, C2, C3, C4, None, None), -1),  # alias
+        ("kv_score_append", (FAKE, FAKE, sh, 10, 0, None, 1, 2 ** 31, 0, ok, C1, C2, C3, C4, None, None), -2),
+        ("kv_score_append", (None, FAKE, sh, 10, 0, None, 1, 0, 0, ok, C1, C2, C3, C4, None, None), -1),   # NULL
     ]
     for fn, args, want in cases:
         rc, msg = _rc(fn, *args)
@@ -104,6 +112,7 @@ def test_validation_rejects_bad_calls_without_launching():
     assert _rc("kv_evict_topk", None, None, sh, 0, 0, ok, None, None, 0, None)[0] == 0
     assert _rc("kv_passthrough_append", None, None, 0, 8, None, None, 0, sh, FAKE, FAKE, FAKE, 8, None)[0] == 0
     assert _rc("qf_filters_from_keys_device", None, 1, 0, 16, 16, 128, None, None, 100, None)[0] == 0
+    assert _rc("kv_score_append", None, None, sh, 0, 0, None, 1, 0, 5, ok, None, None, None, None, None, None)[0] == 0
     n = ctypes.c_size_t(99)
     assert _rc("kv_evict_workspace_size", sh, 64, 1, ok, ctypes.byref(n))[0] == 0 and n.value == 0
 
