@@ -80,10 +80,10 @@ KERNEL_SRC = os.path.join(ROOT, "kv_cache_token_amd", "csrc", "kvx_device.hip")
 # copy) summarised in profiles/, valid only for the kernel source they were
 # taken on (sha256 prefix of kvx_device.hip).
 MEASURED_TRAFFIC = {
-    "c4": {"kernel_src_sha256_16": "9c97df2ed8517956", "bytes_per_launch": 964551490},
-    "c3": {"kernel_src_sha256_16": "9c97df2ed8517956", "bytes_per_launch": 9128278743},
-    "c5": {"kernel_src_sha256_16": "9c97df2ed8517956", "bytes_per_launch": 2204761852},
-    "c2": {"kernel_src_sha256_16": "9c97df2ed8517956", "bytes_per_launch": 122615051},
+    "c4": {"kernel_src_sha256_16": "79c3f6f631ddb13a", "bytes_per_launch": 964555599},
+    "c3": {"kernel_src_sha256_16": "79c3f6f631ddb13a", "bytes_per_launch": 9128278411},
+    "c5": {"kernel_src_sha256_16": "79c3f6f631ddb13a", "bytes_per_launch": 2204763726},
+    "c2": {"kernel_src_sha256_16": "79c3f6f631ddb13a", "bytes_per_launch": 122618569},
 }
 DESCRIPTIONS = {
     "c2": "c2_qfilters_calibrated: 28 layers x 8 KV heads x 128 (224 groups), bf16, one 4096-token block, "
