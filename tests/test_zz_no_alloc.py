@@ -1,8 +1,9 @@
 """The allocation-free selection (kv_evict_topk_noalloc) against kv_evict_topk
 with a caller-allocated workspace, through the C ABI: identical keep_idx on
 two calls in a row, the second smaller than the first, both large enough to
-need the multi-block selection's scratch; a call that needs no scratch; and a
-size whose scratch would exceed the static array, rejected before launch."""
+need the multi-block selection's scratch; a call that needs no scratch; a
+size whose scratch would exceed the static array, rejected before launch; and
+the call captured in a HIP graph and replayed on new scores."""
 import ctypes
 
 import numpy as np
@@ -74,3 +75,42 @@ def test_noalloc_rejects_sizes_beyond_the_scratch_before_launch():
     rc = _lib.lib().kv_evict_topk_noalloc(fake, fake, shape, 1 << 21, 1 << 21, p, fake, None)
     assert rc == _lib.KVX_ERANGE
     assert b"scratch" in _lib.lib().kvx_last_error()
+
+
+def test_noalloc_selection_inside_a_captured_graph():
+    """The use the entry point is for: a selection that needs the multi-block
+    scratch, captured in a HIP graph (nothing allocated during capture) and
+    replayed on new scores written between replays, each replay equal to
+    kv_evict_topk with a caller-allocated workspace."""
+    import torch
+    from kv_cache_token_amd import api
+    G, n_kept, S, budget = 4, 140000, 140000, 140000
+    shape, p = api.make_shape(1, 1, G, "bf16"), api.make_params(budget, 4, 8, "low")
+    need = api.kv_evict_workspace_size(shape, n_kept, S, p)
+    assert need > 0
+    sk = torch.empty((G, budget), device="cuda")
+    sn = torch.empty((G, S), device="cuda")
+    got = torch.empty((G, budget), dtype=torch.int32, device="cuda")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ref = torch.empty_like(got)
+    stream = torch.cuda.Stream()
+    sk.copy_(torch.from_numpy(_scores(G, budget, 40, False)))
+    sn.copy_(torch.from_numpy(_scores(G, S, 41, False)))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):     # first call outside capture: the scratch address is looked up
+        api.kv_evict_topk_noalloc(sk, sn, shape, n_kept, S, p, got, stream=stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        api.kv_evict_topk_noalloc(sk, sn, shape, n_kept, S, p, got, stream=stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        sk.copy_(torch.from_numpy(_scores(G, budget, 50 + rep, rep == 1)))
+        sn.copy_(torch.from_numpy(_scores(G, S, 60 + rep, rep == 1)))
+        got.fill_(-5)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        api.kv_evict_topk(sk, sn, shape, n_kept, S, p, ref, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), "replay %d" % rep
