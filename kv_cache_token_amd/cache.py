@@ -260,6 +260,7 @@ class EvictingCache:
             raise ValueError("cache state was saved with other parameters: %s" % ", ".join(
                 "%s %r (this cache: %r)" % (k, a, b) for k, (a, b) in sorted(diff.items())))
         n = int(meta["n_kept"])
+        self._check_state_arrays(meta, arrays)
         td = api.torch_dtype(self.shape.dtype)
         with torch.cuda.device(self.device):
             if "filters" in arrays:
@@ -287,6 +288,34 @@ class EvictingCache:
             torch.cuda.synchronize(self.device)   # the copies are done before any stream reads them
         self.n_kept, self.tokens_seen = n, int(meta["tokens_seen"])
         self.calib_status = None
+
+    def _check_state_arrays(self, meta: dict, arrays: dict) -> None:
+        """Every array of a state file has the shape and element type the
+        cache's parameters and the saved counts give (ValueError otherwise),
+        so that nothing is broadcast or truncated on the way to the device."""
+        n, seen, calibrating = meta.get("n_kept"), meta.get("tokens_seen"), meta.get("calibrating")
+        cap = self.calib_tokens - 1 if calibrating else self.budget
+        if not (isinstance(n, int) and isinstance(seen, int) and 0 <= n <= cap and n <= seen):
+            raise ValueError("cache state: n_kept %r / tokens_seen %r do not fit this cache (at most %d rows)"
+                             % (n, seen, cap))
+        if calibrating and not (self.mode == "proj" and self.calib_tokens > 0):
+            raise ValueError("cache state holds unscored rows, but this cache does not calibrate")
+        row = np.dtype(np.float32 if self.dtype_name == "f32" else np.uint16)
+        want = {"k": ((self.G, n, self.D), row), "v": ((self.G, n, self.D), row),
+                "pos": ((self.G, n), np.dtype(np.int32))}
+        if not calibrating:
+            want["s"] = ((self.G, n), np.dtype(np.float32))
+        if "filters" in arrays and self.mode == "proj":
+            rows = self.L * self.B if meta.get("per_group_filters") else self.L
+            want["filters"] = ((rows, self.H, self.D), np.dtype(np.float32))
+        extra = sorted(set(arrays) - set(want))
+        if extra:
+            raise ValueError("cache state: unexpected arrays %s" % ", ".join(extra))
+        for name, (shape, dt) in want.items():
+            a = arrays.get(name)
+            if a is None or a.shape != shape or a.dtype != dt:
+                raise ValueError("cache state: %s is %s, expected %s %s" % (
+                    name, "missing" if a is None else "%s %s" % (a.dtype, a.shape), dt, shape))
 
     # -- the step ----------------------------------------------------------
     def _workspace(self, n_kept: int, S: int):

@@ -3,7 +3,8 @@ resumed in a fresh cache (load_state) ends in exactly the state of the
 uninterrupted stream -- kept rows, K/V bytes, stored scores, positions, true
 offset -- for the L2 and projection scorers and for a key-SVD fallback cache
 saved while it still holds unscored rows and after its filters froze; a
-cache with other parameters refuses the file."""
+cache with other parameters, or a file whose arrays do not fit them, is
+refused before anything reaches the device."""
 import numpy as np
 import pytest
 
@@ -130,3 +131,36 @@ def test_state_with_other_parameters_is_refused(tmp_path):
             EvictingCache(**kw).load_state(path)
     with np.load(path, allow_pickle=False) as z:
         assert z["k"].dtype == np.uint16 and z["k"].shape == (4, 64, D) and z["pos"].dtype == np.int32
+
+
+def test_state_whose_arrays_do_not_fit_is_refused(tmp_path):
+    """A state file edited after saving: each array must have the shape and
+    element type its counts give; otherwise load_state raises and the cache
+    keeps its own state."""
+    from kv_cache_token_amd.cache import EvictingCache
+    c = EvictingCache(1, 1, 4, 64, 4, 0, "low", "l2")
+    k, v = _blocks(4, (100,), 5)[0]
+    c.update(k, v)
+    path = str(tmp_path / "s.npz")
+    c.save_state(path)
+    with np.load(path, allow_pickle=False) as z:
+        good = {name: z[name] for name in z.files}
+    edits = [("k", good["k"][:1]),                               # one group, would broadcast
+             ("v", good["v"][:, :10]),                           # fewer rows than n_kept
+             ("pos", good["pos"].astype(np.int64)),               # wrong element type
+             ("s", None),                                         # missing scores
+             ("filters", np.zeros((1, 4, D), np.float32)),        # filters for an L2 cache's state
+             ("meta", np.array(str(good["meta"]).replace('"n_kept": 64', '"n_kept": 65')))]
+    for name, value in edits:
+        bad = dict(good)
+        if value is None:
+            del bad[name]
+        else:
+            bad[name] = value
+        p2 = str(tmp_path / ("bad_%s.npz" % name))
+        with open(p2, "wb") as f:
+            np.savez(f, **bad)
+        fresh = EvictingCache(1, 1, 4, 64, 4, 0, "low", "l2")
+        with pytest.raises(ValueError, match="cache state"):
+            fresh.load_state(p2)
+        assert fresh.n_kept == 0 and fresh.offset == 0
