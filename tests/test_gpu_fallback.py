@@ -9,6 +9,8 @@
   lockstep with FallbackOracleCache (the GPU's filters and scores fed to the
   oracle: kept rows, K/V bytes, stored scores and positions bit for bit), and
   the GPU's filters against the oracle's own estimate.
+* Ragged traffic: sequences fed at different rates, one cache each, freeze at
+  their own calls, interleaved or alone.
 """
 import numpy as np
 import pytest
@@ -311,3 +313,42 @@ def test_failed_estimate_raises_eagerly_and_from_a_plan():
     plan.run()
     with pytest.raises(RuntimeError, match="status 2"):
         plan.check()
+
+
+def test_ragged_sequences_freeze_at_their_own_calls():
+    """Ragged traffic: sequences that receive tokens at different rates each
+    have their own cache (its groups are that sequence's layers x heads, all
+    scored, selected and compacted in the same launches), so each freezes its
+    filters at the call where its own token count crosses calib_tokens.
+    Interleaving the two sequences' calls on one stream leaves each in exactly
+    the state it reaches alone, and alone each is in lockstep with the oracle."""
+    import torch
+    from kv_cache_token_amd.cache import EvictingCache
+    sizes = {"a": [100, 100, 100, 64], "b": [30] * 10 + [200]}
+    seeds = {"a": 41, "b": 42}
+    alone = {n: _lifecycle(2, 1, 4, "bf16", 128, 64, 4, 0, 128, "crossing", sz, seed=seeds[n])[0]
+             for n, sz in sizes.items()}
+    caches, blocks, frozen = {}, {}, {}
+    for n, sz in sizes.items():
+        T = sum(sz)
+        K, V = _aniso(8, T, 128, seeds[n], "bf16"), synth.custom_keys((8, T, 128), seeds[n] + 1, "bf16")
+        starts = np.cumsum([0] + sz)
+        blocks[n] = [(K[:, a:b], V[:, a:b]) for a, b in zip(starts[:-1], starts[1:])]
+        caches[n] = EvictingCache(2, 1, 4, 64, 4, 0, mode="proj", calib_tokens=128)
+    for i in range(max(len(b) for b in blocks.values())):
+        for n in sizes:
+            if i < len(blocks[n]):
+                kb, vb = blocks[n][i]
+                caches[n].update(synth.host_to_torch(np.ascontiguousarray(kb), "bf16").cuda(),
+                                 synth.host_to_torch(np.ascontiguousarray(vb), "bf16").cuda())
+                if not caches[n].calibrating:
+                    frozen.setdefault(n, i)
+    torch.cuda.synchronize()
+    assert frozen == {"a": 1, "b": 4}
+    for n in sizes:
+        c, want = caches[n], alone[n]
+        assert c.offset == want.offset and c.n_kept == want.n_kept
+        assert torch.equal(c.filters, want.filters)
+        for x, y in zip(c.kept(), want.kept()):
+            assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
