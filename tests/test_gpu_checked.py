@@ -1,6 +1,7 @@
 """The checked build (libkvevict_check.so, -DKVX_CHECK): it records nothing on
 valid streams -- the five workloads at full size, compared with the oracle as
-in the full-size tests, and selections on both sides of each on-chip bound --
+in the full-size tests, randomised block streams, and selections on both
+sides of each on-chip bound --
 and it records a corrupt keep_idx handed to the compaction (an index out of
 range, two indices out of order), which the normal build clamps and copies
 without a word."""
@@ -49,6 +50,24 @@ def test_checked_build_is_silent_on_the_workloads(cid, which):
         try:
             _run(cfg, cfg.scorers[which], groups, check_every=64 if cid == 3 else 1)
             torch.cuda.synchronize()
+        finally:
+            api.kvx_check_status_word(None)
+    assert st.cpu().tolist() == [0, 0, 0, 0]
+
+
+def test_checked_build_is_silent_on_random_streams():
+    """The first 100 randomised block streams of the lockstep test (element
+    types, head dims, single tokens, blocks larger than the budget, score
+    ties, sinks and recent windows) through the checked build, each compared
+    with the oracle as there."""
+    from kv_cache_token_amd import _lib, api
+    from tests.test_gpu_random import test_random_stream_lockstep_with_oracle as run_case
+    st = _status()
+    with _lib.checked():
+        api.kvx_check_status_word(st)
+        try:
+            for seed in range(100):
+                run_case(seed)
         finally:
             api.kvx_check_status_word(None)
     assert st.cpu().tolist() == [0, 0, 0, 0]

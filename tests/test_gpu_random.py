@@ -17,7 +17,7 @@ from tests.gpu_util import assert_scores_close, assert_states_equal, gpu_state_a
     oracle_scores, score_scales
 
 pytestmark = pytest.mark.gpu
-N_CASES = 200
+N_CASES = 500
 
 
 @pytest.fixture(scope="module", autouse=True)
