@@ -10,6 +10,9 @@
 
 #include <algorithm>
 #include <array>
+#include <exception>
+#include <mutex>
+#include <new>
 #include <string>
 #include <thread>
 #include <vector>
@@ -152,7 +155,9 @@ double widen_elem(const void *k, int32_t dtype, int64_t i) {
     return f;
 }
 
-// Runs fn(i) for i in [0, n) on up to 16 worker threads.
+// Runs fn(i) for i in [0, n) on up to 16 worker threads.  An exception in a
+// worker (or in starting one) is rethrown here once every started worker
+// has been joined.
 template <class F>
 void parallel_for(int64_t n, F fn) {
     const int64_t hw = std::max(1u, std::thread::hardware_concurrency());
@@ -161,12 +166,41 @@ void parallel_for(int64_t n, F fn) {
         for (int64_t i = 0; i < n; ++i) fn(i);
         return;
     }
-    std::vector<std::thread> th;
-    for (int64_t w = 0; w < nt; ++w)
-        th.emplace_back([=, &fn]() {
+    std::exception_ptr err;
+    std::mutex mu;
+    auto work = [&](int64_t w) {
+        try {
             for (int64_t i = w; i < n; i += nt) fn(i);
-        });
+        } catch (...) {
+            std::lock_guard<std::mutex> lock(mu);
+            if (!err) err = std::current_exception();
+        }
+    };
+    std::vector<std::thread> th;
+    try {
+        for (int64_t w = 0; w < nt; ++w) th.emplace_back(work, w);
+    } catch (...) {
+        for (auto &x : th) x.join();
+        throw;
+    }
     for (auto &x : th) x.join();
+    if (err) std::rethrow_exception(err);
+}
+
+// Runs an entry point's body so that no C++ exception crosses the C ABI: host
+// memory that cannot be had is KVX_ERANGE, anything else the entry point's
+// `code`, each with a message in kvx_last_error().
+template <class F>
+int guarded(const char *what, int code, F &&body) {
+    try {
+        return body();
+    } catch (const std::bad_alloc &) {
+        return set_error(KVX_ERANGE, "%s: out of host memory", what);
+    } catch (const std::exception &e) {
+        return set_error(code, "%s: %s", what, e.what());
+    } catch (...) {
+        return set_error(code, "%s: unexpected failure", what);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -211,7 +245,9 @@ bool parse_npy(const std::string &blob, NpyArray *a) {
     a->descr = h.substr(q1 + 1, q2 - q1 - 1);
     k = field("fortran_order");
     if (k == std::string::npos) return false;
-    a->fortran = h.compare(h.find_first_not_of(" :", k), 4, "True") == 0;
+    const size_t fv = h.find_first_not_of(" :", k);
+    if (fv == std::string::npos) return false;  // the header ends before the value
+    a->fortran = h.compare(fv, 4, "True") == 0;
     k = field("shape");
     if (k == std::string::npos) return false;
     const size_t o = h.find('(', k), c = h.find(')', k);
@@ -414,8 +450,8 @@ KVX_API const char *kvx_last_error(void) { return g_error.c_str(); }
 
 KVX_API int kvx_abi_version(void) { return 1; }
 
-KVX_API int qf_filters_load(const char *path, const char *expect_model_id, int64_t L, int64_t H_kv, int64_t D,
-                            float *out, int64_t *n_samples_out) {
+static int qf_filters_load_body(const char *path, const char *expect_model_id, int64_t L, int64_t H_kv, int64_t D,
+                                float *out, int64_t *n_samples_out) {
     clear_error();
     if (!path || !out || L <= 0 || H_kv <= 0 || D <= 0)
         return set_error(KVX_EINVAL, "qf_filters_load: bad arguments");
@@ -461,8 +497,8 @@ KVX_API int qf_filters_load(const char *path, const char *expect_model_id, int64
     return KVX_OK;
 }
 
-KVX_API int qf_filters_save(const char *path, const float *filters, int64_t L, int64_t H_kv, int64_t D,
-                            const char *model_id, int64_t n_samples, const char *dataset) {
+static int qf_filters_save_body(const char *path, const float *filters, int64_t L, int64_t H_kv, int64_t D,
+                                const char *model_id, int64_t n_samples, const char *dataset) {
     clear_error();
     if (!path || !filters || !model_id || !dataset || L <= 0 || H_kv <= 0 || D <= 0)
         return set_error(KVX_EINVAL, "qf_filters_save: bad arguments");
@@ -508,7 +544,7 @@ KVX_API int qf_filters_save(const char *path, const float *filters, int64_t L, i
     return KVX_OK;
 }
 
-KVX_API int qf_filters_from_queries(const float *q, int64_t H_q, int64_t N, int64_t D, int64_t H_kv, float *out) {
+static int qf_filters_from_queries_body(const float *q, int64_t H_q, int64_t N, int64_t D, int64_t H_kv, float *out) {
     clear_error();
     if (!q || !out || H_q <= 0 || N <= 0 || D <= 0 || D > 4096 || H_kv <= 0)
         return set_error(KVX_EINVAL, "qf_filters_from_queries: bad arguments");
@@ -562,8 +598,8 @@ KVX_API int qf_filters_from_queries(const float *q, int64_t H_q, int64_t N, int6
     return KVX_OK;
 }
 
-KVX_API int qf_filters_from_keys(const void *k, int32_t dtype, int64_t G, int64_t n, int64_t group_stride, int64_t D,
-                                 float *out) {
+static int qf_filters_from_keys_body(const void *k, int32_t dtype, int64_t G, int64_t n, int64_t group_stride,
+                                     int64_t D, float *out) {
     clear_error();
     if (!k || !out || G < 0 || n <= 1 || D <= 0 || D > 4096 || group_stride < n)
         return set_error(KVX_EINVAL, "qf_filters_from_keys: bad arguments");
@@ -617,6 +653,33 @@ KVX_API int kvx_stats(kvx_shape shape, int64_t tokens_seen, int64_t tokens_kept,
     out->compression_ratio = out->kept_bytes ? (double)out->full_seq_bytes / (double)out->kept_bytes : 0.0;
     out->filter_bytes = mode == KVX_SCORE_PROJ ? shape.L * shape.H * shape.D * 4 : 0;
     return KVX_OK;
+}
+
+// The four host entry points that parse files or allocate host memory, each
+// run through guarded() so that a failure is a status, never an exception.
+KVX_API int qf_filters_load(const char *path, const char *expect_model_id, int64_t L, int64_t H_kv, int64_t D,
+                            float *out, int64_t *n_samples_out) {
+    return guarded("qf_filters_load", KVX_EIO, [&] {
+        return qf_filters_load_body(path, expect_model_id, L, H_kv, D, out, n_samples_out);
+    });
+}
+
+KVX_API int qf_filters_save(const char *path, const float *filters, int64_t L, int64_t H_kv, int64_t D,
+                            const char *model_id, int64_t n_samples, const char *dataset) {
+    return guarded("qf_filters_save", KVX_EIO, [&] {
+        return qf_filters_save_body(path, filters, L, H_kv, D, model_id, n_samples, dataset);
+    });
+}
+
+KVX_API int qf_filters_from_queries(const float *q, int64_t H_q, int64_t N, int64_t D, int64_t H_kv, float *out) {
+    return guarded("qf_filters_from_queries", KVX_EINVAL,
+                   [&] { return qf_filters_from_queries_body(q, H_q, N, D, H_kv, out); });
+}
+
+KVX_API int qf_filters_from_keys(const void *k, int32_t dtype, int64_t G, int64_t n, int64_t group_stride, int64_t D,
+                                 float *out) {
+    return guarded("qf_filters_from_keys", KVX_EINVAL,
+                   [&] { return qf_filters_from_keys_body(k, dtype, G, n, group_stride, D, out); });
 }
 
 }  // extern "C"

@@ -203,6 +203,40 @@ def test_corrupt_artifacts_are_rejected(tmp_path):
         assert e.value.code == _lib.KVX_EIO, name
 
 
+def test_malformed_member_headers_are_rejected(tmp_path):
+    """.npy headers cut off inside a field -- no value after 'fortran_order',
+    an unclosed shape, an unclosed descr string -- in members whose CRC-32 is
+    right: the reader refuses them with KVX_EIO (and does not abort)."""
+    import struct
+    import zipfile
+    for name, header in (("fortran_cut", "{'descr': '<f4', 'fortran_order':   "),
+                         ("shape_cut", "{'descr': '<f4', 'fortran_order': False, 'shape': (3, 2, "),
+                         ("descr_cut", "{'descr': '<f4")):
+        h = header.encode("latin-1")
+        p = str(tmp_path / (name + ".npz"))
+        with zipfile.ZipFile(p, "w", zipfile.ZIP_STORED) as z:
+            z.writestr("filters.npy", b"\x93NUMPY\x01\x00" + struct.pack("<H", len(h)) + h)
+        with pytest.raises(KvxError) as e:
+            api.qf_filters_load(p, 3, 2)
+        assert e.value.code == _lib.KVX_EIO and "not a valid .npy" in str(e.value), name
+
+
+@pytest.mark.skipif("asan" in os.environ.get("LD_PRELOAD", ""),
+                    reason="under AddressSanitizer a throwing operator new aborts on exhausted memory")
+def test_host_estimators_report_exhausted_memory_as_a_status():
+    """A host estimate whose working copy cannot be allocated (2^40 rows per
+    head) returns KVX_ERANGE with a message, from the calling thread (one
+    head) and from the worker threads (several heads); the inputs are not
+    read before the allocation."""
+    q = np.zeros(16, dtype=np.float32)
+    out = np.zeros(4 * D, dtype=np.float32)
+    for H_q in (1, 4):
+        rc = _lib.lib().qf_filters_from_queries(q.ctypes.data, H_q, 1 << 40, D, 1, out.ctypes.data)
+        assert rc == _lib.KVX_ERANGE and b"out of host memory" in _lib.lib().kvx_last_error(), H_q
+        rc = _lib.lib().qf_filters_from_keys(q.ctypes.data, _lib.KVX_F32, H_q, 1 << 40, 1 << 40, D, out.ctypes.data)
+        assert rc == _lib.KVX_ERANGE and b"out of host memory" in _lib.lib().kvx_last_error(), H_q
+
+
 def test_query_filters_match_oracle():
     rng = np.random.default_rng(1)
     Hq, N, Hkv = 24, 600, 8
