@@ -343,3 +343,39 @@ def test_library_path_follows_the_environment_override():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, env=env)
     assert out.stdout.split() == [os.path.join(root, "kv_cache_token_amd", "libkvevict.so"),
                                   os.path.join(root, "oracle", "libkvx_oracle.so")]
+
+
+def test_plain_c_caller(tmp_path):
+    """include/kvevict.h compiles as strict C11 and the library links and
+    answers from C (tests/abi_c/abi_check.c): host entry points, and device
+    entry points refusing bad arguments before anything is enqueued."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "abi_check")
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    # a sanitized library (build.py --sanitize) links against the sanitizer runtime it preloads
+    preload = os.environ.get("LD_PRELOAD", "")
+    san_runtime = [preload] if "asan" in preload else []
+    subprocess.check_call([gcc, "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                           "-I", os.path.join(root, "include"), os.path.join(root, "tests", "abi_c", "abi_check.c"),
+                           "-o", exe, "-L", libdir, "-l:" + os.path.basename(_lib.LIB_PATH), "-lm",
+                           "-Wl,-rpath," + libdir] + san_runtime)
+    art = str(tmp_path / "filters.npz")
+    out = subprocess.run([exe, art], capture_output=True, text=True, check=True).stdout
+    got = dict(line.split(" ", 1) for line in out.strip().splitlines())
+    want = {"abi_version": "1", "workspace_rc": "0", "workspace_onchip": "0",
+            "workspace_multiblock": str(224 * (260 + 2 * 128) * 4),
+            "topk_bad_params": str(_lib.KVX_EINVAL), "topk_null_idx": str(_lib.KVX_EINVAL),
+            "score_bad_mode": str(_lib.KVX_EINVAL), "score_proj_no_filters": str(_lib.KVX_EINVAL),
+            "score_bad_head_dim": str(_lib.KVX_EINVAL), "gather_partial_alias": str(_lib.KVX_EINVAL),
+            "decode_position_range": str(_lib.KVX_ERANGE), "last_error_mentions_int32": "1",
+            "save": "0", "load": "0", "load_same": "1", "load_other_model": str(_lib.KVX_EMISMATCH),
+            "load_missing_layer": str(_lib.KVX_EMISMATCH), "from_queries": "0", "from_queries_unit": "1",
+            "from_queries_axis": "1", "stats": "0", "stats_ratio": "8.0"}
+    assert got == want
+    z = np.load(art)
+    assert z["filters"].shape == (2, 2, 4) and str(z["model_id"]) == "org/model" and int(z["n_samples"]) == 7
