@@ -2,7 +2,8 @@
 rows) and a concatenation of KVX_MAX_TOTAL (2^22 rows) per group, through the
 selection with a caller's workspace and the allocation-free one, and through a
 whole evicting call of the cache (multi-block selection, then compaction),
-each compared with the oracle; one row more is refused before launch."""
+each compared with the oracle, and decode steps that shift a whole 2^21-row
+cache in place; one row more is refused before launch."""
 import numpy as np
 import pytest
 
@@ -81,3 +82,33 @@ def test_evicting_call_at_the_largest_budget():
     torch.cuda.synchronize()
     assert c.n_kept == budget and c.offset == 2 * MAX_BUDGET
     assert_states_equal(gpu_state_arrays(c, [0]), lock, [0], "budget 2^21")
+
+
+@pytest.mark.timeout(600)
+def test_decode_at_the_largest_budget():
+    """Single-token calls on a full cache of KVX_MAX_BUDGET rows: each drops
+    one row and shifts up to 2^21 rows down in place (a victim near the front
+    is planted so that almost the whole cache moves), in lockstep with the
+    oracle after every token."""
+    import torch
+    from kv_cache_token_amd.cache import EvictingCache
+    budget, n_sink, recent = MAX_BUDGET, 4, 0
+    say("decode at budget %d" % budget)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    k = torch.randn((1, budget, D), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, budget, D), generator=gen, device="cuda").to(torch.bfloat16)
+    k[0, 10] = 8.0           # the highest norm just after the sinks: evicted first under keep-low
+    c = EvictingCache(1, 1, 1, budget, n_sink, recent, "low", "l2")
+    lock = oracle.OracleCache(1, D, "bf16", budget, n_sink, recent, "low", "l2")
+    c.update(k, v)
+    lock.update(host_rows(k, [0], "bf16"), host_rows(v, [0], "bf16"), scores_in=host_rows(c.last_scores(), [0], "f32"))
+    for t in range(3):
+        kt = torch.randn((1, 1, D), generator=gen, device="cuda").to(torch.bfloat16)
+        vt = torch.randn((1, 1, D), generator=gen, device="cuda").to(torch.bfloat16)
+        c.update(kt, vt)
+        lock.update(host_rows(kt, [0], "bf16"), host_rows(vt, [0], "bf16"),
+                    scores_in=host_rows(c.last_scores(), [0], "f32"))
+        torch.cuda.synchronize()
+        assert_states_equal(gpu_state_arrays(c, [0]), lock, [0], "decode token %d at budget 2^21" % t)
+    assert c.n_kept == budget and c.offset == budget + 3
