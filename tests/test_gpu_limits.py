@@ -85,29 +85,33 @@ def test_evicting_call_at_the_largest_budget():
 
 
 @pytest.mark.timeout(600)
-def test_decode_at_the_largest_budget():
+@pytest.mark.parametrize("dtype,Dd", [("bf16", 128), ("f32", 256)])
+def test_decode_at_the_largest_budget(dtype, Dd):
     """Single-token calls on a full cache of KVX_MAX_BUDGET rows: each drops
     one row and shifts up to 2^21 rows down in place (a victim near the front
     is planted so that almost the whole cache moves), in lockstep with the
-    oracle after every token."""
+    oracle after every token.  With float32 rows of 256 elements a group's K
+    rows span 2 GiB, the most one of the shift's buffer resources covers."""
     import torch
     from kv_cache_token_amd.cache import EvictingCache
     budget, n_sink, recent = MAX_BUDGET, 4, 0
-    say("decode at budget %d" % budget)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    say("decode at budget %d, %s rows of %d" % (budget, dtype, Dd))
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
-    k = torch.randn((1, budget, D), generator=gen, device="cuda").to(torch.bfloat16)
-    v = torch.randn((1, budget, D), generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, budget, Dd), generator=gen, device="cuda").to(td)
+    v = torch.randn((1, budget, Dd), generator=gen, device="cuda").to(td)
     k[0, 10] = 8.0           # the highest norm just after the sinks: evicted first under keep-low
-    c = EvictingCache(1, 1, 1, budget, n_sink, recent, "low", "l2")
-    lock = oracle.OracleCache(1, D, "bf16", budget, n_sink, recent, "low", "l2")
+    c = EvictingCache(1, 1, 1, budget, n_sink, recent, "low", "l2", dtype=dtype, head_dim=Dd)
+    lock = oracle.OracleCache(1, Dd, dtype, budget, n_sink, recent, "low", "l2")
     c.update(k, v)
-    lock.update(host_rows(k, [0], "bf16"), host_rows(v, [0], "bf16"), scores_in=host_rows(c.last_scores(), [0], "f32"))
+    lock.update(host_rows(k, [0], dtype), host_rows(v, [0], dtype), scores_in=host_rows(c.last_scores(), [0], "f32"))
+    del k, v
     for t in range(3):
-        kt = torch.randn((1, 1, D), generator=gen, device="cuda").to(torch.bfloat16)
-        vt = torch.randn((1, 1, D), generator=gen, device="cuda").to(torch.bfloat16)
+        kt = torch.randn((1, 1, Dd), generator=gen, device="cuda").to(td)
+        vt = torch.randn((1, 1, Dd), generator=gen, device="cuda").to(td)
         c.update(kt, vt)
-        lock.update(host_rows(kt, [0], "bf16"), host_rows(vt, [0], "bf16"),
+        lock.update(host_rows(kt, [0], dtype), host_rows(vt, [0], dtype),
                     scores_in=host_rows(c.last_scores(), [0], "f32"))
         torch.cuda.synchronize()
         assert_states_equal(gpu_state_arrays(c, [0]), lock, [0], "decode token %d at budget 2^21" % t)
